@@ -1,0 +1,10 @@
+"""Float64 CPU oracle for absorbed-MLA tree-verify attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library or its binding.
+"""
+from .mla_verify_oracle import (brute_force_verify, chunk_partial, merge_partials, node_scores,
+                                tree_ancestors, verify_attention, visible_positions)
+
+__all__ = ["brute_force_verify", "chunk_partial", "merge_partials", "node_scores",
+           "tree_ancestors", "verify_attention", "visible_positions"]

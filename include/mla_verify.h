@@ -1,0 +1,149 @@
+/*
+ * libmlaverify — tree-verify attention for absorbed-form MLA on MI355X (gfx950).
+ *
+ * The operation (from the pages this library follows):
+ *   - Each cache token j holds a latent kv_c[j] (Dl = 512) and a decoupled RoPE
+ *     key k_pe[j] (Dr = 64), shared by every head; the query is already
+ *     multiplied into latent space ("absorbed"), so query row (b, t, h) brings
+ *     q_nope (512) and q_pe (64).  ["Ground Truth in Silicon" page, "The Message
+ *     in Full" (the reference docstring) and "Input Knowledge Required", item 2]
+ *   - score(j) = scale * (q_nope . kv_c[j] + q_pe . k_pe[j]).
+ *   - Visible keys of tree node t of sequence b: the whole prefix plus the
+ *     tree-tail tokens of t and of its ancestors.  ["Reading the Reference"
+ *     page, "Output Knowledge Created by This Message": prefix visibility +
+ *     tree-tail visibility; "Ground Truth in Silicon" page, "Input Knowledge
+ *     Required", item 3]
+ *   - out = softmax(score) . kv_c over the visible keys (latent-space output;
+ *     the caller applies W_UV), lse = natural-log log-sum-exp of the scaled
+ *     scores.  ["Ground Truth in Silicon" page, "Output Knowledge Created",
+ *     item 1: output aggregation]
+ *   - Long sequences are cut into KV splits whose partial results are merged by
+ *     log-sum-exp (flash-decode).  ["The Information-Gathering Pivot" page,
+ *     "The Context: A Multi-Phase Kernel Integration"]
+ *
+ * Conventions for every entry point:
+ *   - Device pointers point to memory of the current HIP device; host pointers
+ *     are marked "host".  The caller owns every buffer and the stream; the
+ *     library owns only the plan object (host memory).
+ *   - No entry point throws.  Each returns an mla_status; on failure
+ *     mla_verify_last_error() (thread-local) describes the first problem found.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ */
+#ifndef MLA_VERIFY_H_
+#define MLA_VERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* bad size, NULL pointer, misaligned stride ... */
+  MLA_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement */
+  MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the plan needs */
+  MLA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
+
+/* Opaque, immutable after mla_verify_plan(); safe to share between threads. */
+typedef struct mla_verify_plan_s* mla_verify_plan_t;
+
+typedef struct {
+  int32_t batch;            /* B sequences, 1..MLA_VERIFY_MAX_BATCH */
+  int32_t num_heads;        /* H >= 1 */
+  int32_t tree_nodes;       /* T nodes per sequence, 1..64 (one 64-bit mask word) */
+  int32_t d_latent;         /* must be 512 */
+  int32_t d_rope;           /* must be 64 */
+  int32_t dtype;            /* mla_dtype of q_nope, q_pe, kv_c and k_pe; out/lse are fp32 */
+  const int32_t* kv_len_host; /* host [batch]: N_b = P_b + T tokens of sequence b (>= T).
+                                 Read during the call only; sizes the split schedule. */
+  int32_t num_splits;       /* 0 = planner's choice; > 0 forces that many KV splits
+                               for every sequence (capped at its number of key tiles) */
+  int64_t kv_c_row_stride;  /* elements between consecutive kv_c slots (>= 512, multiple of 8) */
+  int64_t k_pe_row_stride;  /* elements between consecutive k_pe slots (>= 64, multiple of 8) */
+} mla_verify_problem;
+
+#define MLA_VERIFY_MAX_BATCH 256
+#define MLA_VERIFY_MAX_TREE 64
+
+typedef struct {
+  int32_t total_splits;     /* sum over sequences of the KV splits */
+  int32_t max_splits;       /* largest split count of one sequence */
+  int32_t rows_per_block;   /* query rows one workgroup processes */
+  int32_t keys_per_tile;    /* keys staged in LDS per step */
+  int32_t grid_blocks;      /* workgroups of the attention launch */
+  int32_t uses_combine;     /* 1 when a split-combine launch follows */
+  size_t workspace_bytes;   /* same value mla_verify_plan() returned */
+} mla_verify_plan_info;
+
+/*
+ * Validate a problem and build its launch plan (host only; no device work).
+ * Checks: sizes above, dtype, strides, kv_len_host[b] >= tree_nodes.
+ * On success *out receives a new plan and *workspace_bytes the device
+ * workspace mla_verify_run() needs (bytes, 256-byte aligned start required).
+ */
+mla_status mla_verify_plan(const mla_verify_problem* problem, mla_verify_plan_t* out,
+                           size_t* workspace_bytes);
+
+/* Describe a plan (host only). */
+mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info* info);
+
+/*
+ * Tree-verify attention of one batch (device work on `stream`, asynchronous).
+ *
+ *   q_nope      device [batch*T, H, 512] of dtype, row-major; row (b*T + t), head h
+ *   q_pe        device [batch*T, H, 64]  of dtype, row-major
+ *   kv_c        device, slot s at kv_c + s*kv_c_row_stride, 512 elements
+ *   k_pe        device, slot s at k_pe + s*k_pe_row_stride, 64 elements
+ *               (kv_c and k_pe may interleave inside one 576-wide buffer)
+ *   kv_indptr   device int32 [batch+1]; kv_indptr[0] = 0 and
+ *               kv_indptr[b+1] - kv_indptr[b] = kv_len_host[b] of the plan
+ *   kv_indices  device int32 [kv_indptr[batch]]: slot of logical position j of
+ *               sequence b at kv_indices[kv_indptr[b] + j] (page_size = 1).
+ *               Positions 0..P_b-1 are the prefix, P_b..P_b+T-1 the tree nodes.
+ *   tree_parents device int32 [batch, T]: parent node of each node, -1 = child
+ *               of the last prefix token; parent[t] < t.  A node whose parent
+ *               chain is invalid gets NaN output rows and lse.
+ *   scale       softmax scale applied to the summed dot products
+ *   out         device fp32 [batch*T, H, 512]
+ *   lse         device fp32 [batch*T, H] (natural log) or NULL
+ *   workspace   device, >= workspace_bytes of the plan, 256-byte aligned.  Holds
+ *               split partials between the two launches; concurrent runs need
+ *               separate workspaces.
+ * No allocation, no host synchronisation and no host reads of device data:
+ * the call only enqueues kernels, so it can be captured in a HIP graph.
+ */
+mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                          const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* tree_parents, float scale,
+                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * Ancestor-or-self bitmask of every tree node (device work on `stream`).
+ *   tree_parents device int32 [batch, tree_nodes], as in mla_verify_run
+ *   masks        device uint64 [batch, tree_nodes]; bit u of masks[b*T + t] is
+ *                set iff node u is t or an ancestor of t.  0 marks an invalid
+ *                parent chain (parent >= node or < -1 somewhere on it).
+ * This is the mask mla_verify_run applies to the tree-tail keys.
+ */
+mla_status mla_verify_tree_masks(const int32_t* tree_parents, int32_t batch, int32_t tree_nodes,
+                                 uint64_t* masks, void* stream);
+
+mla_status mla_verify_plan_destroy(mla_verify_plan_t plan);
+
+/* Static string naming a status code. */
+const char* mla_verify_status_string(mla_status status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* mla_verify_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_VERIFY_H_ */

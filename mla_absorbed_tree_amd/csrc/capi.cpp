@@ -1,0 +1,144 @@
+// extern "C" entry points of libmlaverify: argument checks, plan objects and
+// the launch sequence. Device work happens only inside the launchers.
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/mla_verify.h"
+#include "kernel_params.h"
+#include "plan.h"
+
+struct mla_verify_plan_s {
+  mlav::Plan plan;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_verify_plan(const mla_verify_problem* problem, mla_verify_plan_t* out,
+                           size_t* workspace_bytes) {
+  g_last_error.clear();
+  if (!problem || !out || !workspace_bytes) return fail(MLA_ERR_INVALID_ARG, "NULL argument to mla_verify_plan");
+  *out = nullptr;
+  auto* h = new (std::nothrow) mla_verify_plan_s;
+  if (!h) return fail(MLA_ERR_INVALID_ARG, "out of host memory");
+  std::string err;
+  const mla_status st = mlav::build_plan(*problem, h->plan, err);
+  if (st != MLA_OK) {
+    delete h;
+    return fail(st, err);
+  }
+  *out = h;
+  *workspace_bytes = h->plan.ws_bytes;
+  return MLA_OK;
+}
+
+mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info* info) {
+  if (!plan || !info) return fail(MLA_ERR_INVALID_ARG, "NULL argument to mla_verify_plan_get_info");
+  const mlav::Plan& p = plan->plan;
+  info->total_splits = p.total_splits;
+  info->max_splits = p.max_splits;
+  info->rows_per_block = p.rows_per_block;
+  info->keys_per_tile = mlav::kKeysPerTile;
+  info->grid_blocks = int32_t(p.grid_blocks);
+  info->uses_combine = p.combine ? 1 : 0;
+  info->workspace_bytes = p.ws_bytes;
+  return MLA_OK;
+}
+
+mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                          const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* tree_parents, float scale,
+                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(MLA_ERR_INVALID_ARG, "plan is NULL");
+  const mlav::Plan& p = plan->plan;
+  if (!q_nope || !q_pe || !kv_c || !k_pe || !kv_indptr || !kv_indices || !tree_parents || !out)
+    return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_c) || !aligned16(k_pe) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "q_nope, q_pe, kv_c, k_pe and out must be 16-byte aligned");
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes))
+    return fail(MLA_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
+                                       " bytes is smaller than the plan's " + std::to_string(p.ws_bytes));
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (!(scale == scale)) return fail(MLA_ERR_INVALID_ARG, "scale is NaN");
+
+  mlav::VerifyArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.kv_c = kv_c;
+  a.k_pe = k_pe;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.parents = tree_parents;
+  a.out = out;
+  a.lse = lse;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = p.combine ? reinterpret_cast<float*>(ws + p.ws_part_o) : nullptr;
+  a.part_ml = p.combine ? reinterpret_cast<float*>(ws + p.ws_part_ml) : nullptr;
+  a.kv_c_stride = p.kv_c_stride;
+  a.k_pe_stride = p.k_pe_stride;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.batch = p.batch;
+  a.heads = p.heads;
+  a.tree_nodes = p.tree_nodes;
+  a.rows_per_seq = p.rows_per_seq;
+  a.row_blocks = p.row_blocks;
+  a.total_splits = p.total_splits;
+  for (int b = 0; b <= p.batch; ++b) a.split_offset[b] = p.split_offset[b];
+
+  int e = mlav::launch_verify_attention(a, p.dtype, p.grid_blocks, stream);
+  if (e != 0) return fail(MLA_ERR_HIP, "attention launch failed (hipError " + std::to_string(e) + ")");
+  if (p.combine) {
+    e = mlav::launch_verify_combine(a, stream);
+    if (e != 0) return fail(MLA_ERR_HIP, "combine launch failed (hipError " + std::to_string(e) + ")");
+  }
+  return MLA_OK;
+}
+
+mla_status mla_verify_tree_masks(const int32_t* tree_parents, int32_t batch, int32_t tree_nodes,
+                                 uint64_t* masks, void* stream) {
+  g_last_error.clear();
+  if (!tree_parents || !masks) return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
+  if (batch < 1 || tree_nodes < 1 || tree_nodes > MLA_VERIFY_MAX_TREE)
+    return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 and tree_nodes in 1..64");
+  const int e = mlav::launch_tree_masks(tree_parents, batch, tree_nodes, masks, stream);
+  if (e != 0) return fail(MLA_ERR_HIP, "tree mask launch failed (hipError " + std::to_string(e) + ")");
+  return MLA_OK;
+}
+
+mla_status mla_verify_plan_destroy(mla_verify_plan_t plan) {
+  delete plan;
+  return MLA_OK;
+}
+
+const char* mla_verify_status_string(mla_status status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_verify_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Argument block of the tree-verify kernels (passed by value as kernel arguments).
+#pragma once
+
+#include <cstdint>
+
+#include "../../include/mla_verify.h"
+
+namespace mlav {
+
+struct VerifyArgs {
+  const void* q_nope;          // [B*T, H, 512]
+  const void* q_pe;            // [B*T, H, 64]
+  const void* kv_c;            // slot s at kv_c + s * kv_c_stride
+  const void* k_pe;            // slot s at k_pe + s * k_pe_stride
+  const int32_t* kv_indptr;    // [B + 1]
+  const int32_t* kv_indices;   // page table, page_size = 1
+  const int32_t* parents;      // [B, T]
+  float* out;                  // [B*T, H, 512]
+  float* lse;                  // [B*T, H] or nullptr
+  float* part_o;               // [total_splits, rows_per_seq, 512] (split launches only)
+  float* part_ml;              // [total_splits, rows_per_seq, 2]  (m in log2 units, l)
+  int64_t kv_c_stride;         // elements
+  int64_t k_pe_stride;         // elements
+  float scale_log2;            // softmax scale * log2(e)
+  int32_t batch;
+  int32_t heads;
+  int32_t tree_nodes;
+  int32_t rows_per_seq;        // T * H
+  int32_t row_blocks;          // workgroups along the rows of one sequence
+  int32_t total_splits;
+  int32_t split_offset[MLA_VERIFY_MAX_BATCH + 1];  // first global split of sequence b
+};
+
+// Launchers (defined in the HIP translation unit). Return the launch error.
+int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks, void* stream);
+int launch_verify_combine(const VerifyArgs& a, void* stream);
+int launch_tree_masks(const int32_t* parents, int32_t batch, int32_t tree_nodes, uint64_t* masks,
+                      void* stream);
+
+}  // namespace mlav

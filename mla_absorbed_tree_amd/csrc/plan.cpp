@@ -1,0 +1,135 @@
+// Host-side validation, KV-split schedule and workspace layout.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstdio>
+
+namespace mlav {
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+std::string fmt(const char* f, long long a = 0, long long b = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, f, a, b);
+  return buf;
+}
+
+}  // namespace
+
+mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err) {
+  if (p.batch < 1 || p.batch > MLA_VERIFY_MAX_BATCH) {
+    err = fmt("batch %lld outside 1..%lld", p.batch, MLA_VERIFY_MAX_BATCH);
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (p.num_heads < 1) {
+    err = fmt("num_heads %lld < 1", p.num_heads);
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (p.tree_nodes < 1 || p.tree_nodes > MLA_VERIFY_MAX_TREE) {
+    err = fmt("tree_nodes %lld outside 1..%lld", p.tree_nodes, MLA_VERIFY_MAX_TREE);
+    return p.tree_nodes > MLA_VERIFY_MAX_TREE ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  }
+  if (p.d_latent != kDl || p.d_rope != kDr) {
+    err = fmt("d_latent/d_rope %lld/%lld: only 512/64 is supported", p.d_latent, p.d_rope);
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if (p.dtype != MLA_DTYPE_F32 && p.dtype != MLA_DTYPE_BF16) {
+    err = fmt("unknown dtype %lld", p.dtype);
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (p.kv_c_row_stride < kDl || p.kv_c_row_stride % 8 != 0) {
+    err = fmt("kv_c_row_stride %lld must be >= 512 and a multiple of 8", p.kv_c_row_stride);
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (p.k_pe_row_stride < kDr || p.k_pe_row_stride % 8 != 0) {
+    err = fmt("k_pe_row_stride %lld must be >= 64 and a multiple of 8", p.k_pe_row_stride);
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (p.num_splits < 0) {
+    err = fmt("num_splits %lld < 0", p.num_splits);
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (!p.kv_len_host) {
+    err = "kv_len_host is NULL";
+    return MLA_ERR_INVALID_ARG;
+  }
+  const int64_t rows_per_seq = int64_t(p.tree_nodes) * p.num_heads;
+  if (rows_per_seq > (int64_t(1) << 24)) {
+    err = fmt("tree_nodes * num_heads = %lld is too large", rows_per_seq);
+    return MLA_ERR_INVALID_ARG;
+  }
+
+  plan = Plan();
+  plan.batch = p.batch;
+  plan.heads = p.num_heads;
+  plan.tree_nodes = p.tree_nodes;
+  plan.dtype = p.dtype;
+  plan.kv_c_stride = p.kv_c_row_stride;
+  plan.k_pe_stride = p.k_pe_row_stride;
+  plan.rows_per_seq = int32_t(rows_per_seq);
+  plan.rows_per_block = p.dtype == MLA_DTYPE_BF16 ? kRowsPerBlockBf16 : kRowsPerBlockF32;
+  plan.row_blocks = (plan.rows_per_seq + plan.rows_per_block - 1) / plan.rows_per_block;
+
+  plan.kv_len.resize(p.batch);
+  int64_t total_tiles = 0;
+  std::vector<int64_t> tiles(p.batch);
+  for (int b = 0; b < p.batch; ++b) {
+    const int32_t n = p.kv_len_host[b];
+    if (n < p.tree_nodes) {
+      err = fmt("kv_len_host[%lld] = %lld is smaller than tree_nodes", b, n);
+      return MLA_ERR_INVALID_ARG;
+    }
+    plan.kv_len[b] = n;
+    tiles[b] = (int64_t(n) + kKeysPerTile - 1) / kKeysPerTile;
+    total_tiles += tiles[b];
+  }
+
+  // Split schedule. Forced: S_b = min(num_splits, tiles_b). Automatic: pick a
+  // chunk length (in tiles) so that the launch holds about one workgroup per
+  // compute unit, but never chunks shorter than kMinChunkTiles (a split's
+  // partial write costs about as much as a few tiles of compute).
+  constexpr int64_t kMinChunkTiles = 8;
+  plan.splits.resize(p.batch);
+  if (p.num_splits > 0) {
+    for (int b = 0; b < p.batch; ++b)
+      plan.splits[b] = int32_t(std::min<int64_t>(p.num_splits, tiles[b]));
+  } else {
+    const int64_t work = int64_t(plan.row_blocks) * total_tiles;
+    if (int64_t(plan.row_blocks) * p.batch >= kComputeUnits) {
+      std::fill(plan.splits.begin(), plan.splits.end(), 1);
+    } else {
+      const int64_t chunk = std::max<int64_t>(kMinChunkTiles, (work + kComputeUnits - 1) / kComputeUnits);
+      for (int b = 0; b < p.batch; ++b)
+        plan.splits[b] = int32_t(std::max<int64_t>(1, (tiles[b] + chunk - 1) / chunk));
+    }
+  }
+  plan.split_offset.assign(p.batch + 1, 0);
+  for (int b = 0; b < p.batch; ++b) {
+    plan.split_offset[b + 1] = plan.split_offset[b] + plan.splits[b];
+    plan.max_splits = std::max(plan.max_splits, plan.splits[b]);
+    if (plan.splits[b] > 1) plan.combine = true;
+  }
+  plan.total_splits = plan.split_offset[p.batch];
+  plan.chunk_groups = (plan.total_splits + kXcds - 1) / kXcds;
+  plan.grid_blocks = int64_t(plan.chunk_groups) * kXcds * plan.row_blocks;
+  if (plan.grid_blocks > (int64_t(1) << 31) - 1) {
+    err = "launch grid too large";
+    return MLA_ERR_UNSUPPORTED;
+  }
+
+  size_t off = 256;  // status flags live in the first 256 bytes
+  plan.ws_status = 0;
+  if (plan.combine) {
+    const size_t part_rows = size_t(plan.total_splits) * size_t(plan.rows_per_seq);
+    plan.ws_part_ml = off;
+    off = align_up(off + part_rows * 2 * sizeof(float), 256);
+    plan.ws_part_o = off;
+    off = align_up(off + part_rows * kDl * sizeof(float), 256);
+  }
+  plan.ws_bytes = off;
+  return MLA_OK;
+}
+
+}  // namespace mlav

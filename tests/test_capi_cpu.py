@@ -1,0 +1,108 @@
+"""Host-side checks of libmlaverify: it loads, exports what the header declares,
+and its planner validates problems and sizes workspaces (no device work)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_verify.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    lib = os.path.join(ROOT, "mla_absorbed_tree_amd", "libmlaverify.so")
+    if not os.path.exists(lib):
+        from mla_absorbed_tree_amd.build_lib import build
+        build()
+    from mla_absorbed_tree_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_verify_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols(B):
+    assert declared_functions() == sorted(B.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(B):
+    lib = ctypes.CDLL(B.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(B):
+    assert B.mla_verify_status_string(0) == "MLA_OK"
+    assert B.mla_verify_status_string(-3) == "MLA_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), -1), (dict(batch=257), -1), (dict(num_heads=0), -1),
+    (dict(tree_nodes=0), -1), (dict(tree_nodes=65), -2), (dict(d_latent=256), -2),
+    (dict(d_rope=32), -2), (dict(dtype=7), -1), (dict(kv_c_row_stride=500), -1),
+    (dict(kv_c_row_stride=516), -1), (dict(k_pe_row_stride=60), -1), (dict(num_splits=-1), -1),
+    (dict(kv_len_host=[10, 3]), -1)])
+def test_plan_rejects_bad_problems(B, kw, status):
+    args = dict(batch=2, num_heads=4, tree_nodes=8, dtype=1, kv_len_host=[100, 50])
+    args.update(kw)
+    if "batch" in kw and kw["batch"] > 0:
+        args["kv_len_host"] = [100] * kw["batch"]
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_plan(**args)
+    assert e.value.status == status
+    assert B.mla_verify_last_error() != ""
+
+
+def test_forced_and_auto_split_schedules(B):
+    p, ws = B.mla_verify_plan(1, 64, 32, 1, [200032], num_splits=256)
+    info = B.mla_verify_plan_get_info(p)
+    assert info["total_splits"] == 256 and info["uses_combine"] == 1
+    rows = 32 * 64
+    assert info["grid_blocks"] == 256 * (rows // 128)
+    assert ws >= 256 * rows * (512 + 2) * 4
+    B.mla_verify_plan_destroy(p)
+    # more splits than key tiles are capped at the tile count
+    p, _ = B.mla_verify_plan(2, 4, 4, 1, [40, 100], num_splits=50)
+    info = B.mla_verify_plan_get_info(p)
+    assert info["total_splits"] == 2 + 4
+    B.mla_verify_plan_destroy(p)
+    # a problem with many row blocks needs no split: no combine, no partials
+    p, ws = B.mla_verify_plan(16, 64, 64, 1, [5000] * 16)
+    info = B.mla_verify_plan_get_info(p)
+    assert info["total_splits"] == 16 and info["uses_combine"] == 0 and ws == 256
+    B.mla_verify_plan_destroy(p)
+    # fp32 uses 32-row blocks
+    p, _ = B.mla_verify_plan(1, 16, 8, 0, [264], num_splits=1)
+    assert B.mla_verify_plan_get_info(p)["rows_per_block"] == 32
+    B.mla_verify_plan_destroy(p)
+
+
+def test_run_argument_checks_happen_before_any_launch(B):
+    p, ws = B.mla_verify_plan(1, 64, 16, 1, [4112], num_splits=4)
+    fake = 1 << 20  # never dereferenced: every call below fails validation first
+    args = [fake] * 7
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_run(p, *args, 0.1, fake, fake, fake, ws - 1, stream=0)
+    assert e.value.status == B.MLA_ERR_WORKSPACE
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_run(p, *args, 0.1, fake, fake, fake + 64, ws, stream=0)
+    assert e.value.status == B.MLA_ERR_WORKSPACE   # misaligned workspace
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_run(p, fake, 0, *args[2:], 0.1, fake, fake, fake, ws, stream=0)
+    assert e.value.status == B.MLA_ERR_INVALID_ARG
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_run(p, fake + 4, *args[1:], 0.1, fake, fake, fake, ws, stream=0)
+    assert e.value.status == B.MLA_ERR_INVALID_ARG  # misaligned q_nope
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_run(p, *args, float("nan"), fake, fake, fake, ws, stream=0)
+    assert e.value.status == B.MLA_ERR_INVALID_ARG
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_tree_masks(fake, 1, 65, fake, stream=0)
+    assert e.value.status == B.MLA_ERR_INVALID_ARG
+    B.mla_verify_plan_destroy(p)

@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of tree-verify attention (libmlaverify) on one MI355X.
+
+One step = one pass of the whole path (tree masks + split-KV attention + LSE
+combine, i.e. mla_verify_attend followed by mla_verify_combine) over one batch
+of synthetic inputs that already sit in HBM. The primary workload is the
+32k-prefix batch (B=4, H=64, P=32768, T=64, bf16); the 200k-prefix workload
+(B=1, H=64, P=200000, T=32, 256 splits) is reported in "also".
+
+Prints ONE JSON line. `value` is KV tokens/s (sum of N_b per step / step time);
+`roofline` describes the attention kernel (algorithmic FLOPs per launch over
+its average HIP-event duration, against the dense bf16 MFMA peak);
+`cpu_baseline` is the float64 oracle timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify attn KV tokens/s and achieved HBM GB/s / MFMA % at 32k and 200k prefix"
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+PRIMARY = "b4_h64_p32768_t64_bf16"
+ALSO = "b1_h64_p200000_t32_bf16_s256"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def tree_depths(parents_row):
+    """Number of ancestor-or-self nodes of each tree node (parent[t] < t)."""
+    d = np.zeros(len(parents_row), dtype=np.int64)
+    for t, p in enumerate(parents_row):
+        d[t] = 1 + (d[p] if p >= 0 else 0)
+    return d
+
+
+def algorithmic_counts(x):
+    """FLOPs and HBM bytes one step must do, from the workload alone.
+
+    FLOPs = 2 * H * (576 + 512) per visible (query row, key) pair; a node of
+    sequence b sees P_b prefix keys plus its ancestors-or-self.
+    Bytes = KV (576 elements per token) + page-table entries + Q + out/lse +
+    parents; split partials are not algorithmic and are counted apart.
+    """
+    cfg = x.cfg
+    e = 2 if cfg.dtype == "bf16" else 4
+    H, T = cfg.heads, cfg.tree_nodes
+    pairs = 0
+    for b in range(cfg.batch):
+        pairs += T * int(x.prefix_lens[b]) + int(tree_depths(x.parents[b]).sum())
+    flops = 2.0 * H * (576 + 512) * pairs
+    kv_tokens = int(x.kv_lens.sum())
+    rows = cfg.batch * T * H
+    bytes_ = kv_tokens * 576 * e + kv_tokens * 4 + rows * 576 * e + rows * 513 * 4 + cfg.batch * T * 4
+    return flops, bytes_, kv_tokens, pairs
+
+
+def bench_workload(name, steps, warmup, num_splits=None):
+    import torch
+    from gen import get_config, make_inputs
+    from mla_absorbed_tree_amd import binding as B
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+
+    cfg = get_config(name)
+    log("[bench] generating %s" % name)
+    x = make_inputs(cfg)
+    flops, bytes_, kv_tokens, pairs = algorithmic_counts(x)
+    d = device_inputs(x)
+    splits = cfg.num_splits if num_splits is None else num_splits
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, splits)
+    rows = cfg.batch * cfg.tree_nodes
+    out = torch.empty((rows, cfg.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows, cfg.heads), dtype=torch.float32, device="cuda")
+    args = (d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"], d["kv_indices"],
+            d["tree_parents"], x.scale, out, lse, mv.workspace)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        B.mla_verify_attend(mv.plan, *args)
+        if ev is not None:
+            ev[1].record()
+        B.mla_verify_combine(mv.plan, out, lse, mv.workspace)
+        if ev is not None:
+            ev[2].record()
+
+    log("[bench] %s plan=%s warmup=%d steps=%d" % (name, mv.info, warmup, steps))
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    step_ms = wall / steps * 1e3
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    achieved = flops / (attn_ms * 1e-3)
+    res = {
+        "workload": name,
+        "value": kv_tokens / (step_ms * 1e-3),
+        "ms_per_step": step_ms,
+        "kv_tokens": kv_tokens,
+        "visible_pairs_per_s": pairs * cfg.heads / (step_ms * 1e-3),
+        "hbm_gbps": bytes_ / (step_ms * 1e-3) / 1e9,
+        "hbm_frac": bytes_ / (step_ms * 1e-3) / PEAK_HBM_BYTES,
+        "mfma_frac": flops / (step_ms * 1e-3) / PEAK_BF16_FLOPS,
+        "kernels_ms": {"attention": attn_ms, "combine": comb_ms},
+        "plan": mv.info,
+        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS, "traffic": None,
+                     "kernel": "mla_verify_attn_kernel<bf16>",
+                     "flops_per_launch": flops, "avg_launch_ms": attn_ms},
+        "config": {"workload": name, "batch": cfg.batch, "heads": cfg.heads,
+                   "prefix": cfg.prefix if cfg.prefix is not None else list(cfg.prefix_range),
+                   "tree_nodes": cfg.tree_nodes, "kv_layout": cfg.layout,
+                   "num_splits": mv.info["total_splits"] // cfg.batch if cfg.batch == 1 else "auto",
+                   "d_latent": 512, "d_rope": 64, "kv_dtype": cfg.dtype, "out_dtype": "f32"},
+    }
+    mv.close()
+    del d
+    torch.cuda.empty_cache()
+    return res, x
+
+
+def cpu_baseline(x, budget_s=15.0):
+    """Time the float64 oracle on a bounded sample of the workload's nodes and
+    scale to the whole step (KV tokens/s)."""
+    from oracle import verify_attention
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    cfg = x.cfg
+    order = [(b, t) for t in range(cfg.tree_nodes) for b in range(cfg.batch)]
+
+    def run(nodes):
+        t0 = time.perf_counter()
+        verify_attention(x.q_nope, x.q_pe, x.kv_c, x.k_pe, x.kv_indptr, x.kv_indices, x.parents,
+                         x.scale, nodes=nodes)
+        return time.perf_counter() - t0
+
+    first = run(order[:1])
+    n = int(min(len(order), max(1, budget_s / max(first, 1e-3))))
+    took = run(order[:n])
+    full = took / n * len(order)
+    return {"value": float(x.kv_lens.sum()) / full, "unit": "KV tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": "%d of %d tree nodes (all %d heads each) of %s in %.1f s; full step "
+                      "extrapolated to %.1f s" % (n, len(order), cfg.heads, cfg.name, took, full)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=PRIMARY)
+    ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--no-also", action="store_true", help="skip the 200k-prefix workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    res, x = bench_workload(a.workload, a.steps, a.warmup, a.num_splits)
+    also = []
+    if not a.no_also and a.workload != ALSO:
+        r2, _ = bench_workload(ALSO, a.steps, a.warmup)
+        also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "hbm_gbps", "hbm_frac",
+                                        "mfma_frac", "kernels_ms", "roofline", "config", "plan")})
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on a bounded sample")
+        cpu = cpu_baseline(x, a.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": res["value"],
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": res["config"],
+        "hbm_gbps": res["hbm_gbps"],
+        "hbm_frac": res["hbm_frac"],
+        "mfma_frac": res["mfma_frac"],
+        "kernels_ms": res["kernels_ms"],
+        "plan": res["plan"],
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -124,6 +124,24 @@ mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void
                           void* stream);
 
 /*
+ * The two halves of mla_verify_run, for callers that schedule or time them
+ * separately. mla_verify_attend takes exactly the arguments of mla_verify_run
+ * and enqueues the attention kernel: sequences with one KV split write out/lse
+ * directly, the others leave per-split partials (m, l, O) in the workspace.
+ * mla_verify_combine then merges those partials by log-sum-exp into out/lse
+ * (it enqueues nothing when the plan has no split sequence). Calling attend and
+ * then combine on one stream with the same workspace equals mla_verify_run.
+ */
+mla_status mla_verify_attend(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                             const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* tree_parents, float scale,
+                             float* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+mla_status mla_verify_combine(mla_verify_plan_t plan, float* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Ancestor-or-self bitmask of every tree node (device work on `stream`).
  *   tree_parents device int32 [batch, tree_nodes], as in mla_verify_run
  *   masks        device uint64 [batch, tree_nodes]; bit u of masks[b*T + t] is

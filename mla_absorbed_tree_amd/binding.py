@@ -27,6 +27,7 @@ MLA_VERIFY_MAX_TREE = 64
 
 # Symbols declared in include/mla_verify.h.
 EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
+                    "mla_verify_attend", "mla_verify_combine",
                     "mla_verify_tree_masks", "mla_verify_plan_destroy",
                     "mla_verify_status_string", "mla_verify_last_error")
 
@@ -64,6 +65,8 @@ def _load():
     lib.mla_verify_plan_get_info.argtypes = [vp, ctypes.POINTER(mla_verify_plan_info)]
     lib.mla_verify_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                    ctypes.c_size_t, vp]
+    lib.mla_verify_attend.argtypes = lib.mla_verify_run.argtypes
+    lib.mla_verify_combine.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.mla_verify_tree_masks.argtypes = [vp, i32, i32, vp, vp]
     lib.mla_verify_plan_destroy.argtypes = [vp]
     lib.mla_verify_status_string.argtypes = [i32]
@@ -71,7 +74,8 @@ def _load():
     lib.mla_verify_last_error.argtypes = []
     lib.mla_verify_last_error.restype = ctypes.c_char_p
     for name in ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
-                 "mla_verify_tree_masks", "mla_verify_plan_destroy"):
+                 "mla_verify_attend", "mla_verify_combine", "mla_verify_tree_masks",
+                 "mla_verify_plan_destroy"):
         getattr(lib, name).restype = i32
     del i64
     return lib
@@ -153,6 +157,27 @@ def mla_verify_run(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_p
                                _ptr(kv_indptr), _ptr(kv_indices), _ptr(tree_parents),
                                float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                int(workspace_bytes), _stream_handle(stream)))
+
+
+def mla_verify_attend(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents,
+                      scale: float, out, lse, workspace, workspace_bytes: Optional[int] = None,
+                      stream=None) -> None:
+    """Enqueue only the attention kernel (split sequences leave partials in the workspace)."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.mla_verify_attend(plan, _ptr(q_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe),
+                                  _ptr(kv_indptr), _ptr(kv_indices), _ptr(tree_parents),
+                                  float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  int(workspace_bytes), _stream_handle(stream)))
+
+
+def mla_verify_combine(plan, out, lse, workspace, workspace_bytes: Optional[int] = None,
+                       stream=None) -> None:
+    """Enqueue the log-sum-exp merge of the split partials (no-op without splits)."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.mla_verify_combine(plan, _ptr(out), _ptr(lse), _ptr(workspace),
+                                   int(workspace_bytes), _stream_handle(stream)))
 
 
 def mla_verify_tree_masks(tree_parents, batch: int, tree_nodes: int, masks, stream=None) -> None:

@@ -59,18 +59,23 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
   return MLA_OK;
 }
 
-mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
-                          const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
-                          const int32_t* kv_indices, const int32_t* tree_parents, float scale,
-                          float* out, float* lse, void* workspace, size_t workspace_bytes,
-                          void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Checks the run arguments and fills the kernel argument block.
+mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe, const void* kv_c,
+                   const void* k_pe, const int32_t* kv_indptr, const int32_t* kv_indices,
+                   const int32_t* tree_parents, float scale, float* out, float* lse,
+                   void* workspace, size_t workspace_bytes, bool need_inputs, mlav::VerifyArgs& a) {
   if (!plan) return fail(MLA_ERR_INVALID_ARG, "plan is NULL");
   const mlav::Plan& p = plan->plan;
-  if (!q_nope || !q_pe || !kv_c || !k_pe || !kv_indptr || !kv_indices || !tree_parents || !out)
+  if (need_inputs && (!q_nope || !q_pe || !kv_c || !k_pe || !kv_indptr || !kv_indices || !tree_parents))
     return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
-  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_c) || !aligned16(k_pe) || !aligned16(out))
-    return fail(MLA_ERR_INVALID_ARG, "q_nope, q_pe, kv_c, k_pe and out must be 16-byte aligned");
+  if (!out) return fail(MLA_ERR_INVALID_ARG, "out is NULL");
+  if (need_inputs && (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_c) || !aligned16(k_pe)))
+    return fail(MLA_ERR_INVALID_ARG, "q_nope, q_pe, kv_c and k_pe must be 16-byte aligned");
+  if (!aligned16(out)) return fail(MLA_ERR_INVALID_ARG, "out must be 16-byte aligned");
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes))
     return fail(MLA_ERR_WORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
                                        " bytes is smaller than the plan's " + std::to_string(p.ws_bytes));
@@ -78,7 +83,6 @@ mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void
     return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (!(scale == scale)) return fail(MLA_ERR_INVALID_ARG, "scale is NaN");
 
-  mlav::VerifyArgs a;
   std::memset(&a, 0, sizeof a);
   a.q_nope = q_nope;
   a.q_pe = q_pe;
@@ -102,14 +106,62 @@ mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void
   a.row_blocks = p.row_blocks;
   a.total_splits = p.total_splits;
   for (int b = 0; b <= p.batch; ++b) a.split_offset[b] = p.split_offset[b];
-
-  int e = mlav::launch_verify_attention(a, p.dtype, p.grid_blocks, stream);
-  if (e != 0) return fail(MLA_ERR_HIP, "attention launch failed (hipError " + std::to_string(e) + ")");
-  if (p.combine) {
-    e = mlav::launch_verify_combine(a, stream);
-    if (e != 0) return fail(MLA_ERR_HIP, "combine launch failed (hipError " + std::to_string(e) + ")");
-  }
   return MLA_OK;
+}
+
+mla_status launch_attend(const mlav::Plan& p, const mlav::VerifyArgs& a, void* stream) {
+  const int e = mlav::launch_verify_attention(a, p.dtype, p.grid_blocks, stream);
+  if (e != 0) return fail(MLA_ERR_HIP, "attention launch failed (hipError " + std::to_string(e) + ")");
+  return MLA_OK;
+}
+
+mla_status launch_combine(const mlav::Plan& p, const mlav::VerifyArgs& a, void* stream) {
+  if (!p.combine) return MLA_OK;
+  const int e = mlav::launch_verify_combine(a, stream);
+  if (e != 0) return fail(MLA_ERR_HIP, "combine launch failed (hipError " + std::to_string(e) + ")");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                          const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* tree_parents, float scale,
+                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_last_error.clear();
+  mlav::VerifyArgs a;
+  mla_status st = prepare(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents, scale,
+                          out, lse, workspace, workspace_bytes, true, a);
+  if (st != MLA_OK) return st;
+  st = launch_attend(plan->plan, a, stream);
+  if (st != MLA_OK) return st;
+  return launch_combine(plan->plan, a, stream);
+}
+
+mla_status mla_verify_attend(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                             const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* tree_parents, float scale,
+                             float* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_last_error.clear();
+  mlav::VerifyArgs a;
+  const mla_status st = prepare(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents,
+                                scale, out, lse, workspace, workspace_bytes, true, a);
+  if (st != MLA_OK) return st;
+  return launch_attend(plan->plan, a, stream);
+}
+
+mla_status mla_verify_combine(mla_verify_plan_t plan, float* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mlav::VerifyArgs a;
+  const mla_status st = prepare(plan, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                0.f, out, lse, workspace, workspace_bytes, false, a);
+  if (st != MLA_OK) return st;
+  return launch_combine(plan->plan, a, stream);
 }
 
 mla_status mla_verify_tree_masks(const int32_t* tree_parents, int32_t batch, int32_t tree_nodes,

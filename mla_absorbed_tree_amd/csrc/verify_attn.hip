@@ -5,23 +5,28 @@
 // weighted sum of kv_c (latent-space output) and the log-sum-exp.
 //
 // Work decomposition: one workgroup per (sequence b, block of query rows, KV
-// split). A KV tile of 32 keys (kv_c | k_pe, 1152 B per key in bf16) is staged
-// in LDS once and serves every query row of the block: 128 rows (4 waves x 32)
-// in bf16, so a head-shared latent is read from L2 once per 128 rows instead
-// of once per head (the "64x redundant reads" of a per-head kernel).
+// split). Every key tile (kv_c | k_pe) is staged in LDS once and serves all
+// query rows of the block, so the head-shared latent is read from L2 once per
+// block instead of once per head.
 //
-// Per wave, per 32-key step (bf16):
-//   S^T[32 keys x 32 rows] = K[32 x 576] . Q^T      36 x mfma_f32_32x32x16_bf16
-//       A = K from LDS (ds_read_b128), B = Q held in VGPRs for the whole split
-//   online softmax on S^T in fp32 (exp2 domain), P rounded to bf16
-//   O^T[512 x 32 rows] += V^T[512 x 32] . P^T       32 x mfma_f32_32x32x16_bf16
-//       A = V^T via ds_read_b64_tr_b16 from the same LDS tile, B = P^T from VGPRs
-// O^T lives in 256 accumulation registers per lane (16 blocks of 32x32 fp32).
+// bf16 kernel: 4 waves, 128 query rows, 32-key tiles.
+//   * A 4-deep LDS ring of key tiles is filled by global_load_lds_dwordx4
+//     (global -> LDS without registers), 3 tiles ahead of the tile in use.
+//   * QK: wave w owns query rows 32w..32w+31 and keeps their Q (576 bf16) in
+//     VGPRs. S^T[32 keys x 32 rows] = K . Q^T with 36 mfma_f32_32x32x16_bf16.
+//   * Softmax weights in fp32 (exp2 domain) against a per-row reference max,
+//     rounded to bf16 and shared through LDS (P, 8 KB per tile).
+//   * PV: wave w owns output features 128w..128w+127 of all 128 rows:
+//     O^T[128 x 128] += V^T . P^T with 32 MFMAs; V^T comes from the same LDS
+//     tile through ds_read_b64_tr_b16, P^T with plain 16-byte LDS reads.
+//     Splitting PV by features (not rows) cuts the transpose reads, whose LDS
+//     rate is a third of plain reads, by 4x.
+//   * O^T lives in 256 accumulation registers per lane.
 // The key order inside each 16-deep MFMA step is permuted consistently in P^T
 // and V^T so that P^T comes straight from the S^T accumulator layout.
 //
-// The fp32 instance (parity workloads in fp32) keeps the same structure with
-// mfma_f32_32x32x2_f32, one wave of 32 rows, and Q staged in LDS.
+// fp32 kernel (parity workloads stored in fp32): 1 wave, 32 rows, one LDS tile,
+// mfma_f32_32x32x2_f32, Q staged in LDS; same softmax and epilogue rules.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -40,6 +45,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
 
 constexpr float kLn2 = 0.693147180559945309f;
 // Largest excess (log2 units) of a score over the row's reference max that a
@@ -57,6 +64,23 @@ __device__ __forceinline__ float shfl_f32(float v, int src_lane) {
 }
 // Value held by the lane in the other half of the wave (lane ^ 32).
 __device__ __forceinline__ float swap_halves(float v) { return shfl_f32(v, lane_id() ^ 32); }
+
+// s_waitcnt with only the vector-memory counter bounded (<= N outstanding).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// s_waitcnt lgkmcnt(0): this wave's LDS reads/writes are complete.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also drain every outstanding global->LDS load). Callers wait for exactly the
+// counters they need first.
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Ancestor-or-self mask of tree node `lane` (lanes >= T return 0), by pointer
 // doubling over the parent array: after r rounds a node has OR-ed the masks of
@@ -88,6 +112,13 @@ __device__ __forceinline__ uint64_t wave_tree_mask(const int32_t* __restrict__ p
   return bad ? 0ull : ((uint64_t)hi << 32) | lo;
 }
 
+// Mask of `node` fetched from the lane that built it.
+__device__ __forceinline__ uint64_t node_mask(uint64_t tmask, int node) {
+  const uint32_t lo = (uint32_t)shfl_i32((int)(uint32_t)tmask, node);
+  const uint32_t hi = (uint32_t)shfl_i32((int)(uint32_t)(tmask >> 32), node);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __global__ void __launch_bounds__(64) mla_tree_masks_kernel(const int32_t* __restrict__ parents, int T,
                                                             uint64_t* __restrict__ masks) {
   const int b = blockIdx.x;
@@ -95,165 +126,401 @@ __global__ void __launch_bounds__(64) mla_tree_masks_kernel(const int32_t* __res
   if (lane_id() < T) masks[(int64_t)b * T + lane_id()] = m;
 }
 
-template <bool kF32>
-struct KCfg;
-template <>
-struct KCfg<false> {
-  static constexpr int kWaves = 4;
-  static constexpr int kEsz = 2;
-};
-template <>
-struct KCfg<true> {
-  static constexpr int kWaves = 1;
-  static constexpr int kEsz = 4;
-};
-
-template <bool kF32>
-struct KLayout {
-  static constexpr int kWaves = KCfg<kF32>::kWaves;
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kRows = 32 * kWaves;
-  static constexpr int kEsz = KCfg<kF32>::kEsz;
-  // One LDS row per key: kv_c | k_pe, plus 16 B of padding so that the 32
-  // keys read by one MFMA operand load start in different banks.
-  static constexpr int kRowBytes = kDk * kEsz + 16;
-  static constexpr int kTileBytes = kKeysPerTile * kRowBytes;
-  static constexpr int kQBytes = kF32 ? 32 * kRowBytes : 0;
-  static constexpr int kSmemBytes = kTileBytes + kQBytes;
+// ---------------------------------------------------------------------------
+// Workgroup -> (sequence, KV split, row block), XCD-aware.
+// Consecutive workgroup ids are dealt to different XCDs; every row block of
+// one KV chunk gets the same XCD so the chunk streams through a single L2.
+// ---------------------------------------------------------------------------
+struct BlockWork {
+  int b, s, S, c, rb;
+  int kv0, N, P;
+  int tile_begin, tile_end;
+  bool seq_ok;
 };
 
-// Stage keys [k0, k0 + 32) of sequence b into LDS (rows past N are zero).
-template <bool kF32>
-__device__ __forceinline__ void stage_tile(const VerifyArgs& a, char* smem, int kv0, int k0, int N) {
-  using L = KLayout<kF32>;
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  if constexpr (!kF32) {
-    // Wave w stages keys 8w..8w+7: each kv_c row (1 KB) is one 64-lane
-    // 16-byte load; the eight 128-byte k_pe rows together are another.
-    const int kfirst = wave * 8;
-    const int jl = k0 + kfirst + (lane & 7);
-    int my_slot = 0;
-    if (lane < 8 && jl < N) my_slot = a.kv_indices[kv0 + jl];
-    const __bf16* kvc = (const __bf16*)a.kv_c;
-    const __bf16* kpe = (const __bf16*)a.k_pe;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int key = kfirst + kk;
-      const int slot = __builtin_amdgcn_readlane(my_slot, kk);
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (k0 + key < N) v = *(const u32x4_t*)(kvc + (int64_t)slot * a.kv_c_stride + lane * 8);
-      *(u32x4_t*)(smem + key * L::kRowBytes + lane * 16) = v;
-    }
-    {
-      const int kk = lane >> 3, ch = lane & 7;
-      const int key = kfirst + kk;
-      const int slot = shfl_i32(my_slot, kk);
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (k0 + key < N) v = *(const u32x4_t*)(kpe + (int64_t)slot * a.k_pe_stride + ch * 8);
-      *(u32x4_t*)(smem + key * L::kRowBytes + kDl * 2 + ch * 16) = v;
-    }
-  } else {
-    // One wave stages all 32 keys: kv_c rows are 2 KB (two loads each), four
-    // 256-byte k_pe rows per load.
-    const int jl = k0 + (lane & 31);
-    int my_slot = 0;
-    if (lane < 32 && jl < N) my_slot = a.kv_indices[kv0 + jl];
-    const float* kvc = (const float*)a.kv_c;
-    const float* kpe = (const float*)a.k_pe;
-#pragma unroll 4
-    for (int key = 0; key < kKeysPerTile; ++key) {
-      const int slot = __builtin_amdgcn_readlane(my_slot, key);
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (k0 + key < N)
-          v = *(const u32x4_t*)(kvc + (int64_t)slot * a.kv_c_stride + part * 256 + lane * 4);
-        *(u32x4_t*)(smem + key * L::kRowBytes + part * 1024 + lane * 16) = v;
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int key = g * 4 + (lane >> 4), ch = lane & 15;
-      const int slot = shfl_i32(my_slot, key);
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (k0 + key < N) v = *(const u32x4_t*)(kpe + (int64_t)slot * a.k_pe_stride + ch * 4);
-      *(u32x4_t*)(smem + key * L::kRowBytes + kDl * 4 + ch * 16) = v;
-    }
-  }
-}
-
-template <bool kF32>
-__global__ void __launch_bounds__(KLayout<kF32>::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mla_verify_attn_kernel(const VerifyArgs a) {
-  using L = KLayout<kF32>;
-  __shared__ __attribute__((aligned(16))) char smem[L::kSmemBytes];
-
-  // ---- workgroup -> (row block, global split), XCD-aware -------------------
-  // Consecutive workgroup ids go to different XCDs; give every row block of one
-  // KV chunk the same XCD so the chunk streams through a single L2.
+__device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w) {
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int local = bid / kXcds;
-  const int rb = local % a.row_blocks;
-  const int c = (local / a.row_blocks) * kXcds + xcd;
-  if (c >= a.total_splits) return;
+  w.rb = local % a.row_blocks;
+  w.c = (local / a.row_blocks) * kXcds + xcd;
+  if (w.c >= a.total_splits) return false;
   int lo = 0, hi = a.batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (a.split_offset[mid] <= c) lo = mid;
+    if (a.split_offset[mid] <= w.c) lo = mid;
     else hi = mid - 1;
   }
-  const int b = lo;
-  const int S = a.split_offset[b + 1] - a.split_offset[b];
-  const int s = c - a.split_offset[b];
+  w.b = lo;
+  w.S = a.split_offset[w.b + 1] - a.split_offset[w.b];
+  w.s = w.c - a.split_offset[w.b];
+  w.kv0 = a.kv_indptr[w.b];
+  w.N = a.kv_indptr[w.b + 1] - w.kv0;
+  w.P = w.N - a.tree_nodes;
+  w.seq_ok = w.P >= 0;
+  const int ntiles = w.seq_ok ? (w.N + kKeysPerTile - 1) / kKeysPerTile : 0;
+  w.tile_begin = (int)(((int64_t)w.s * ntiles) / w.S);
+  w.tile_end = (int)(((int64_t)(w.s + 1) * ntiles) / w.S);
+  return true;
+}
 
+// Masks and scales the 16 scores this lane holds in an S^T block and returns
+// the row max over the 32 keys. Register i holds key k0 + (i/4)*8 + 4*half +
+// i%4. Prefix keys are visible; tail key P+u iff bit u of anc; keys >= N are
+// padding.
+__device__ __forceinline__ float mask_scale_max(float (&sv)[16], const f32x16_t& sacc, float scale_log2,
+                                                int k0, int half, int P, int N, uint64_t anc) {
+  const bool no_mask = k0 + kKeysPerTile <= P;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int j = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
+    const bool tail_bit = ((anc >> ((j - P) & 63)) & 1ull) != 0;
+    const bool vis = no_mask | (j < P) | ((j < N) & tail_bit);
+    sv[i] = vis ? sacc[i] * scale_log2 : -INFINITY;
+    mx = fmaxf(mx, sv[i]);
+  }
+  return fmaxf(mx, swap_halves(mx));
+}
+
+// ===========================================================================
+// bf16 kernel
+// ===========================================================================
+namespace bf16k {
+constexpr int kThreads = 256;
+constexpr int kRows = 128;
+constexpr int kNbuf = 4;                        // LDS ring of key tiles
+constexpr int kAhead = kNbuf - 1;               // tiles in flight ahead of the one in use
+constexpr int kCRow = kDl * 2 + 32;             // padded kv_c row: 1056 B
+constexpr int kCBytes = kKeysPerTile * kCRow;   // kv_c part of a tile
+constexpr int kPeRow = kDr * 2;                 // 128 B, 16-byte chunks XOR-swizzled by key
+constexpr int kBufBytes = kCBytes + kKeysPerTile * kPeRow;  // 37888
+constexpr int kPBytes = kRows * kKeysPerTile * 2;           // 8192
+// Page-table entries of upcoming tiles also travel global -> LDS, into a ring
+// of kIdxRing tiles; they are fetched kIdxLead tiles before the keys they name.
+constexpr int kIdxRing = 4;
+constexpr int kIdxLead = 3;
+constexpr int kIdxBytes = kIdxRing * kKeysPerTile * 4;      // 512
+constexpr int kSmem = kNbuf * kBufBytes + kPBytes + kIdxBytes;
+// Vector-memory instructions each wave issues per tile: 8 kv_c rows, one
+// block of 8 k_pe rows, one block of 8 page-table entries.
+constexpr int kVmemPerTile = 10;
+static_assert(kSmem <= 160 * 1024, "LDS budget");
+}  // namespace bf16k
+
+// One global_load_lds_dword issued by lanes 0..7 of the wave: the page-table
+// entries of this wave's 8 keys of `tile` land in ring slot tile % kIdxRing.
+// Positions past `jmax` (the split's last key) are clamped to it: those keys
+// are loaded but either masked out of the softmax (past the sequence) or
+// never computed (past the split), and their data is a real, finite token.
+__device__ __forceinline__ void issue_tile_index(const VerifyArgs& a, char* idx_ring, int kv0, int jmax,
+                                                 int tile) {
+  using namespace bf16k;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  if (lane < 8) {
+    const int j = min(tile * kKeysPerTile + wave * 8 + lane, jmax);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(
+            idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8) * 4));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(base),
+                 "v"((uint64_t)(a.kv_indices + kv0 + j))
+                 : "memory", "m0");
+  }
+}
+
+// Slots of this wave's 8 keys of `tile` (lane & 7 -> key), read back from the
+// index ring once this wave's load of them has completed.
+__device__ __forceinline__ int tile_slots(const char* idx_ring, int tile) {
+  using namespace bf16k;
+  const int wave = threadIdx.x >> 6;
+  return *(const int*)(idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8 + (lane_id() & 7)) * 4);
+}
+
+// One global_load_lds_dwordx4: lane i copies 16 bytes from its `src` to LDS
+// byte address lds_base + 16*i. Issued as inline asm so that the compiler's
+// own wait insertion does not treat every later LDS read as dependent on it
+// (which would drain the whole prefetch ring); the kernel waits for these
+// loads explicitly with wait_vmem<>. Vector-memory loads retire in order, so
+// the compiler's waits for its own loads stay correct.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"((uint64_t)src)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Enqueue this wave's share of one tile into LDS buffer `buf`: keys 8w..8w+7.
+// Each kv_c row (1 KB) is one 64-lane 16-byte load; the eight 128-byte k_pe
+// rows together are another, lane i fetching chunk (i%8) ^ (i/8) so that the
+// chunks of one key land XOR-swizzled by the key index.
+__device__ __forceinline__ void issue_tile(const VerifyArgs& a, char* buf, int slots) {
+  using namespace bf16k;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const __bf16* kvc = (const __bf16*)a.kv_c;
+  const uint32_t base = lds_addr(buf);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int slot = __builtin_amdgcn_readlane(slots, kk);
+    lds_dma16(kvc + (int64_t)slot * a.kv_c_stride + lane * 8, base + (wave * 8 + kk) * kCRow);
+  }
+  const int slot = shfl_i32(slots, lane >> 3);
+  const int chunk = (lane & 7) ^ (lane >> 3);
+  lds_dma16((const __bf16*)a.k_pe + (int64_t)slot * a.k_pe_stride + chunk * 8,
+            base + kCBytes + wave * 8 * kPeRow);
+}
+
+__global__ void __launch_bounds__(bf16k::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_verify_attn_bf16_kernel(const VerifyArgs a) {
+  using namespace bf16k;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  char* const pbuf = smem + kNbuf * kBufBytes;
+  char* const idx_ring = pbuf + kPBytes;
+
+  BlockWork w;
+  if (!map_block(a, w)) return;
   const int T = a.tree_nodes, H = a.heads;
-  const int kv0 = a.kv_indptr[b];
-  const int N = a.kv_indptr[b + 1] - kv0;
-  const int P = N - T;
-  const bool seq_ok = P >= 0;
-  const int ntiles = seq_ok ? (N + kKeysPerTile - 1) / kKeysPerTile : 0;
-  const int tile_begin = (int)(((int64_t)s * ntiles) / S);
-  const int tile_end = (int)(((int64_t)(s + 1) * ntiles) / S);
 
-  // ---- this lane's query row ------------------------------------------------
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;     // which 8-wide k slice / which key quartets
-  const int qcol = lane & 31;     // query column of the 32x32 blocks
-  const int r_local = rb * L::kRows + wave * 32 + qcol;
-  const bool row_ok = r_local < a.rows_per_seq;
-  const int r_eff = row_ok ? r_local : a.rows_per_seq - 1;
-  const int node = r_eff / H;
-  const int64_t grow = (int64_t)b * a.rows_per_seq + r_eff;
+  const int half = lane >> 5;   // k slice of MFMA operands / key quartet of S^T rows
+  const int qcol = lane & 31;   // column of the 32x32 blocks
 
-  const uint64_t tmask = wave_tree_mask(a.parents + (int64_t)b * T, T);
-  const uint32_t anc_lo = (uint32_t)shfl_i32((int)(uint32_t)tmask, node);
-  const uint32_t anc_hi = (uint32_t)shfl_i32((int)(uint32_t)(tmask >> 32), node);
-  const uint64_t anc = ((uint64_t)anc_hi << 32) | anc_lo;
-  const bool node_ok = seq_ok && anc != 0;
+  // ---- QK role: this lane's query row (wave owns rows 32w..32w+31) ---------
+  const int r_local = w.rb * kRows + wave * 32 + qcol;
+  const int r_eff = min(r_local, a.rows_per_seq - 1);
+  const int64_t grow = (int64_t)w.b * a.rows_per_seq + r_eff;
+  const uint64_t tmask = wave_tree_mask(a.parents + (int64_t)w.b * T, T);
+  const uint64_t anc = node_mask(tmask, r_eff / H);
+  const bool node_ok = w.seq_ok && anc != 0;
 
-  // ---- Q --------------------------------------------------------------------
-  bf16x8_t qreg[kF32 ? 1 : 36];
-  if constexpr (!kF32) {
+  bf16x8_t qreg[36];
+  {
     const __bf16* qn = (const __bf16*)a.q_nope + grow * kDl + half * 8;
     const __bf16* qp = (const __bf16*)a.q_pe + grow * kDr + half * 8;
 #pragma unroll
     for (int kc = 0; kc < 32; ++kc) qreg[kc] = *(const bf16x8_t*)(qn + kc * 16);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) qreg[32 + kc] = *(const bf16x8_t*)(qp + kc * 16);
-  } else {
-    // Q rows of the wave into LDS: row qr = [q_nope | q_pe] in fp32.
-    char* qs = smem + L::kTileBytes;
-    for (int idx = lane; idx < 32 * 144; idx += 64) {
-      const int qr = idx / 144, ch = idx % 144;
-      const int rr = min(rb * L::kRows + qr, a.rows_per_seq - 1);
-      const int64_t gr = (int64_t)b * a.rows_per_seq + rr;
-      const float* src = ch < 128 ? (const float*)a.q_nope + gr * kDl + ch * 4
-                                  : (const float*)a.q_pe + gr * kDr + (ch - 128) * 4;
-      *(u32x4_t*)(qs + qr * L::kRowBytes + ch * 16) = *(const u32x4_t*)src;
+  }
+
+  // Per-lane LDS address pieces.
+  // K (A operand of QK): key = qcol, 8 features at 16*kc + 8*half.
+  const int k_off = qcol * kCRow + half * 16;
+  const int kpe_off = kCBytes + qcol * kPeRow;
+  const int kpe_sw = qcol & 7;
+  // V^T (A operand of PV) via transpose reads: 16-lane group g reads 4 keys x
+  // 16 features; lane i of the group points at key 4*half + i/4, features
+  // 16*(g%2) + 4*(i%4) of this wave's feature range.
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int v_off = (4 * half + (i16 >> 2)) * kCRow + (16 * (g16 & 1) + 4 * (i16 & 3)) * 2 + wave * 4 * 64;
+
+  // Softmax state of this lane's row (same rules as the fp32 kernel):
+  // m_ref = reference max (log2 units, scaled) fixed at the first tile where
+  // the row sees a key; weights are 2^(s - m_ref); if some score exceeds it by
+  // more than kOverflowSlack the block repeats the split with the exact max.
+  f32x16_t oacc[16];  // [f4 * 4 + rb]: feature block 4*wave + f4, row block rb
+  float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int x = 0; x < 16; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
+    l_run = 0.f;
+    bool overflow = false;
+
+    if (w.tile_begin < w.tile_end) {
+      const int tb = w.tile_begin, te = w.tile_end;
+      // Pipeline: iteration t computes tile t, enqueues the keys of tile
+      // t+kAhead and the page-table entries of tile t+kAhead+kIdxLead. Tiles
+      // past the split repeat its last key (loaded, never computed), which
+      // keeps the number of loads per iteration constant.
+      const int jmax = min(w.N, te * kKeysPerTile) - 1;
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) issue_tile_index(a, idx_ring, w.kv0, jmax, tb + i);
+      wait_vmem<0>();
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) {
+        issue_tile(a, smem + ((tb + i) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + i));
+        issue_tile_index(a, idx_ring, w.kv0, jmax, tb + i + kIdxLead);
+      }
+
+      for (int tile = tb; tile < te; ++tile) {
+        // Loads issued after this wave's keys of `tile`: its index block plus
+        // kAhead-1 later iterations. Waiting down to that count also lands the
+        // index block of tile+kAhead (issued kIdxLead iterations ago).
+        static_assert(kIdxLead == kAhead, "wait count below assumes equal leads");
+        wait_vmem<kVmemPerTile * (kAhead - 1)>();
+        block_sync();  // the whole tile is in LDS; every wave has finished tile-1
+        const char* buf = smem + (tile % kNbuf) * kBufBytes;
+        issue_tile(a, smem + ((tile + kAhead) % kNbuf) * kBufBytes, tile_slots(idx_ring, tile + kAhead));
+        issue_tile_index(a, idx_ring, w.kv0, jmax, tile + kAhead + kIdxLead);
+        const int k0 = tile * kKeysPerTile;
+
+        // ---- S^T = K . Q^T (this wave's 32 rows) ---------------------------
+        // Batches of four MFMAs with the next batch's LDS reads in flight; the
+        // scheduling barriers stop the compiler from hoisting every read.
+        f32x16_t sacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+        {
+          bf16x8_t kf[2][4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) kf[0][j] = *(const bf16x8_t*)(buf + k_off + j * 32);
+#pragma unroll
+          for (int kb = 0; kb < 9; ++kb) {
+            if (kb + 1 < 9) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int kc = 4 * (kb + 1) + j;
+                const char* p = kc < 32 ? buf + k_off + kc * 32
+                                        : buf + kpe_off + (((2 * (kc - 32) + half) ^ kpe_sw) << 4);
+                kf[(kb + 1) & 1][j] = *(const bf16x8_t*)p;
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], qreg[4 * kb + j], sacc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+
+        // ---- mask, scale, weights -----------------------------------------
+        float sv[16];
+        const float mx = mask_scale_max(sv, sacc, a.scale_log2, k0, half, w.P, w.N, anc);
+        m_max = fmaxf(m_max, mx);
+        if (m_ref == -INFINITY) m_ref = mx;
+        overflow |= mx > m_ref + kOverflowSlack;
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+          psum += sv[i];
+        }
+        l_run += psum;
+        // P^T operand fragments of this wave's rows go to LDS for all waves.
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t pk;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) pk[jj] = (__bf16)sv[8 * u + jj];
+          *(bf16x8_t*)(pbuf + ((wave * 2 + u) * 64 + lane) * 16) = pk;
+        }
+        wait_lds();
+        block_sync();
+
+        // ---- O^T[this wave's 128 features x 128 rows] += V^T . P^T ---------
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t pb[4];
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) pb[rb] = *(const bf16x8_t*)(pbuf + ((rb * 2 + u) * 64 + lane) * 16);
+#pragma unroll
+          for (int f4 = 0; f4 < 4; ++f4) {
+            const char* vp = buf + v_off + (16 * u) * kCRow + f4 * 64;
+            const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vp);
+            const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 8 * kCRow));
+            const bf16x8_t vf =
+                __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+              oacc[f4 * 4 + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[rb], oacc[f4 * 4 + rb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      wait_vmem<0>();
     }
+    if (!__syncthreads_or(overflow)) break;
+    m_ref = m_max;
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  // Row statistics travel from the QK owner of each row to every wave.
+  const float l_tot = l_run + swap_halves(l_run);
+  __syncthreads();
+  float2* stats = (float2*)pbuf;
+  if (half == 0) stats[wave * 32 + qcol] = make_float2(node_ok ? m_ref : NAN, l_tot);
+  __syncthreads();
+  // Accumulator register i of block (f4, rb) holds feature
+  // 32*(4*wave + f4) + (i/4)*8 + 4*half + i%4 of row 32*rb + qcol.
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int r = w.rb * kRows + rb * 32 + qcol;
+    if (r >= a.rows_per_seq) continue;
+    const float2 st = stats[rb * 32 + qcol];
+    const bool ok = !(st.x != st.x);
+    const int64_t g = (int64_t)w.b * a.rows_per_seq + r;
+    float* dst;
+    float mul;
+    if (w.S == 1) {
+      dst = a.out + g * kDl;
+      mul = ok ? 1.f / st.y : NAN;
+      if (wave == 0 && half == 0 && a.lse) a.lse[g] = ok ? (st.x + __log2f(st.y)) * kLn2 : NAN;
+    } else {
+      const int64_t prow = (int64_t)w.c * a.rows_per_seq + r;
+      dst = a.part_o + prow * kDl;
+      mul = 1.f;
+      if (wave == 0 && half == 0) {
+        a.part_ml[2 * prow] = st.x;
+        a.part_ml[2 * prow + 1] = ok ? st.y : NAN;
+      }
+    }
+#pragma unroll
+    for (int f4 = 0; f4 < 4; ++f4)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = oacc[f4 * 4 + rb][4 * gi + e] * mul;
+        *(f32x4_t*)(dst + 32 * (4 * wave + f4) + 8 * gi + 4 * half) = v;
+      }
+  }
+}
+
+// ===========================================================================
+// fp32 kernel
+// ===========================================================================
+namespace f32k {
+constexpr int kThreads = 64;
+constexpr int kRows = 32;
+constexpr int kRowBytes = kDk * 4 + 16;                 // kv_c | k_pe, padded
+constexpr int kTileBytes = kKeysPerTile * kRowBytes;
+constexpr int kSmem = kTileBytes + kRows * kRowBytes;   // tile + Q rows
+}  // namespace f32k
+
+__global__ void __launch_bounds__(f32k::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_verify_attn_f32_kernel(const VerifyArgs a) {
+  using namespace f32k;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  char* const qs = smem + kTileBytes;
+
+  BlockWork w;
+  if (!map_block(a, w)) return;
+  const int T = a.tree_nodes, H = a.heads;
+  const int lane = lane_id();
+  const int half = lane >> 5;
+  const int qcol = lane & 31;
+  const int r_local = w.rb * kRows + qcol;
+  const bool row_ok = r_local < a.rows_per_seq;
+  const int r_eff = row_ok ? r_local : a.rows_per_seq - 1;
+  const int64_t grow = (int64_t)w.b * a.rows_per_seq + r_eff;
+  const uint64_t tmask = wave_tree_mask(a.parents + (int64_t)w.b * T, T);
+  const uint64_t anc = node_mask(tmask, r_eff / H);
+  const bool node_ok = w.seq_ok && anc != 0;
+
+  // Q rows of the block into LDS: row qr = [q_nope | q_pe].
+  for (int idx = lane; idx < kRows * 144; idx += 64) {
+    const int qr = idx / 144, ch = idx % 144;
+    const int rr = min(w.rb * kRows + qr, a.rows_per_seq - 1);
+    const int64_t gr = (int64_t)w.b * a.rows_per_seq + rr;
+    const float* src = ch < 128 ? (const float*)a.q_nope + gr * kDl + ch * 4
+                                : (const float*)a.q_pe + gr * kDr + (ch - 128) * 4;
+    *(u32x4_t*)(qs + qr * kRowBytes + ch * 16) = *(const u32x4_t*)src;
   }
 
   // Softmax state of this lane's row. m_ref is the reference max (log2 units,
@@ -263,173 +530,113 @@ mla_verify_attn_kernel(const VerifyArgs a) {
   // the whole workgroup repeats the split once with m_ref = the exact max of
   // the split (m_max), which cannot overflow.
   f32x16_t oacc[16];
-  float m_ref = -INFINITY;
-  float m_max = -INFINITY;
-  float l_run = 0.f;        // this lane's partial denominator (its 16 keys of each step)
-
-  // Per-lane pieces of the LDS addresses (see the layout notes at the top).
-  const char* k_rd = smem + qcol * L::kRowBytes + half * (kF32 ? 4 : 16);
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const char* v_rd = smem + (4 * half + (i16 >> 2)) * L::kRowBytes + (16 * (g16 & 1) + 4 * (i16 & 3)) * 2;
+  float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
+  const float* k_rd = (const float*)(smem + qcol * kRowBytes) + half;
+  const float* q_rd = (const float*)(qs + qcol * kRowBytes) + half;
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int fb = 0; fb < 16; ++fb)
+    for (int fb = 0; fb < 16; ++fb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[fb][i] = 0.f;
-  l_run = 0.f;
-  bool overflow = false;
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const int k0 = tile * kKeysPerTile;
-    __syncthreads();
-    stage_tile<kF32>(a, smem, kv0, k0, N);
-    __syncthreads();
-
-    // ---- S^T = K . Q^T ------------------------------------------------------
-    // Issued in batches of four MFMAs with the next batch's LDS reads in
-    // flight; the scheduling barriers keep the compiler from hoisting every
-    // read at once (which would not fit next to Q and O in registers).
-    f32x16_t sacc;
+      for (int i = 0; i < 16; ++i) oacc[fb][i] = 0.f;
+    l_run = 0.f;
+    bool overflow = false;
+    for (int tile = w.tile_begin; tile < w.tile_end; ++tile) {
+      const int k0 = tile * kKeysPerTile;
+      __syncthreads();
+      {
+        // Stage keys k0..k0+31: kv_c rows are 2 KB (two loads each), four
+        // 256-byte k_pe rows per load. Past-the-end keys repeat the last token.
+        const int my_slot = a.kv_indices[w.kv0 + min(k0 + (lane & 31), w.N - 1)];
+        const float* kvc = (const float*)a.kv_c;
+        const float* kpe = (const float*)a.k_pe;
+#pragma unroll 4
+        for (int key = 0; key < kKeysPerTile; ++key) {
+          const int slot = __builtin_amdgcn_readlane(my_slot, key);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    if constexpr (!kF32) {
-      bf16x8_t kf[2][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kf[0][j] = *(const bf16x8_t*)(k_rd + j * 32);
-#pragma unroll
-      for (int kb = 0; kb < 9; ++kb) {
-        if (kb + 1 < 9) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) kf[(kb + 1) & 1][j] = *(const bf16x8_t*)(k_rd + (4 * (kb + 1) + j) * 32);
+          for (int part = 0; part < 2; ++part)
+            *(u32x4_t*)(smem + key * kRowBytes + part * 1024 + lane * 16) =
+                *(const u32x4_t*)(kvc + (int64_t)slot * a.kv_c_stride + part * 256 + lane * 4);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], qreg[4 * kb + j], sacc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int g = 0; g < 8; ++g) {
+          const int key = g * 4 + (lane >> 4), ch = lane & 15;
+          const int slot = shfl_i32(my_slot, key);
+          *(u32x4_t*)(smem + key * kRowBytes + kDl * 4 + ch * 16) =
+              *(const u32x4_t*)(kpe + (int64_t)slot * a.k_pe_stride + ch * 4);
+        }
       }
-    } else {
-      const float* kp = (const float*)k_rd;
-      const float* qp = (const float*)(smem + L::kTileBytes + qcol * L::kRowBytes) + half;
+      __syncthreads();
+
+      f32x16_t sacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll 8
       for (int kc = 0; kc < kDk / 2; ++kc)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kp[2 * kc], qp[2 * kc], sacc, 0, 0, 0);
-    }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k_rd[2 * kc], q_rd[2 * kc], sacc, 0, 0, 0);
 
-    // ---- scale, tree mask, softmax weights -----------------------------------
-    // Register i of this lane holds key (i/4)*8 + 4*half + i%4 of the tile.
-    float sv[16];
-    const bool no_mask = k0 + kKeysPerTile <= P;
-    float mx = -INFINITY;
+      float sv[16];
+      const float mx = mask_scale_max(sv, sacc, a.scale_log2, k0, half, w.P, w.N, anc);
+      m_max = fmaxf(m_max, mx);
+      if (m_ref == -INFINITY) m_ref = mx;
+      overflow |= mx > m_ref + kOverflowSlack;
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
-      // Branch-free: prefix keys are visible, tail key P+u iff bit u of anc.
-      const bool tail_bit = ((anc >> ((j - P) & 63)) & 1ull) != 0;
-      const bool vis = no_mask | (j < P) | ((j < N) & tail_bit);
-      sv[i] = vis ? sacc[i] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[i]);
-    }
-    mx = fmaxf(mx, swap_halves(mx));
-    m_max = fmaxf(m_max, mx);
-    if (m_ref == -INFINITY) m_ref = mx;
-    overflow |= mx > m_ref + kOverflowSlack;
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
-      psum += sv[i];
-    }
-    l_run += psum;
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+        psum += sv[i];
+      }
+      l_run += psum;
 
-    // ---- O^T += V^T . P^T -----------------------------------------------------
-    if constexpr (!kF32) {
-      bf16x8_t pk[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pk[u][jj] = (__bf16)sv[8 * u + jj];
-      // 8 batches: (u, four output blocks); V^T operands via transpose reads.
-      i16x4_t vf[2][4][2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vf[0][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(v_rd + j * 64));
-        vf[0][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(v_rd + 8 * L::kRowBytes + j * 64));
-      }
-#pragma unroll
-      for (int bt = 0; bt < 8; ++bt) {
-        const int u = bt >> 2, fb0 = (bt & 3) * 4;
-        if (bt + 1 < 8) {
-          const int un = (bt + 1) >> 2, fbn = ((bt + 1) & 3) * 4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vf[(bt + 1) & 1][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(v_rd + (16 * un) * L::kRowBytes + (fbn + j) * 64));
-            vf[(bt + 1) & 1][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(v_rd + (16 * un + 8) * L::kRowBytes + (fbn + j) * 64));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const i16x8_t v01 = __builtin_shufflevector(vf[bt & 1][j][0], vf[bt & 1][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[fb0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v01), pk[u],
-                                                                  oacc[fb0 + j], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
+      // O^T[512 x 32 rows] += V^T . P^T: step i pairs key (i/4)*8 + i%4
+      // (lanes 0-31) with key (i/4)*8 + 4 + i%4 (lanes 32-63).
 #pragma unroll
       for (int fb = 0; fb < 16; ++fb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = (i >> 2) * 8 + 4 * half + (i & 3);
-          const float v = ((const float*)(smem + key * L::kRowBytes))[32 * fb + qcol];
+          const float v = ((const float*)(smem + key * kRowBytes))[32 * fb + qcol];
           oacc[fb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, sv[i], oacc[fb], 0, 0, 0);
         }
       }
     }
+    if (!__syncthreads_or(overflow)) break;
+    m_ref = m_max;
   }
 
-  if (!__syncthreads_or(overflow)) break;
-  m_ref = m_max;
-  }
-
-  // ---- epilogue ---------------------------------------------------------------
   // Accumulator register i of block fb holds feature 32*fb + (i/4)*8 + 4*half + i%4.
   const float l_tot = l_run + swap_halves(l_run);
   if (!row_ok) return;
-  if (S == 1) {
-    const float inv = node_ok ? 1.f / l_tot : NAN;
-    float* orow = a.out + grow * kDl + 4 * half;
-#pragma unroll
-    for (int fb = 0; fb < 16; ++fb)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        f32x4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = oacc[fb][4 * gi + e] * inv;
-        *(f32x4_t*)(orow + 32 * fb + 8 * gi) = v;
-      }
+  float* dst;
+  float mul;
+  if (w.S == 1) {
+    dst = a.out + grow * kDl;
+    mul = node_ok ? 1.f / l_tot : NAN;
     if (half == 0 && a.lse) a.lse[grow] = node_ok ? (m_ref + __log2f(l_tot)) * kLn2 : NAN;
   } else {
-    const int64_t prow = (int64_t)c * a.rows_per_seq + r_eff;
-    float* po = a.part_o + prow * kDl + 4 * half;
-#pragma unroll
-    for (int fb = 0; fb < 16; ++fb)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        f32x4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = oacc[fb][4 * gi + e];
-        *(f32x4_t*)(po + 32 * fb + 8 * gi) = v;
-      }
+    const int64_t prow = (int64_t)w.c * a.rows_per_seq + r_eff;
+    dst = a.part_o + prow * kDl;
+    mul = 1.f;
     if (half == 0) {
       a.part_ml[2 * prow] = node_ok ? m_ref : NAN;
       a.part_ml[2 * prow + 1] = node_ok ? l_tot : NAN;
     }
   }
+#pragma unroll
+  for (int fb = 0; fb < 16; ++fb)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      f32x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = oacc[fb][4 * gi + e] * mul;
+      *(f32x4_t*)(dst + 32 * fb + 8 * gi + 4 * half) = v;
+    }
 }
 
+// ===========================================================================
+// Split combine
+// ===========================================================================
 // Merge the split partials of one query row (a workgroup of 128 lanes, 4
 // features per lane): M = max m_c, w_c = 2^(m_c - M), L = sum w_c l_c,
 // out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Empty splits (m = -inf) add
@@ -440,6 +647,7 @@ constexpr int kCombineStage = 256;
 __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(const VerifyArgs a) {
   __shared__ float wsh[kCombineStage];
   __shared__ float red[kCombineThreads / 64];
+  __shared__ int nan_sh[kCombineThreads / 64];
   const int64_t grow = blockIdx.x;
   const int b = (int)(grow / a.rows_per_seq);
   const int r = (int)(grow % a.rows_per_seq);
@@ -462,7 +670,6 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
     mloc = fmaxf(mloc, shfl_f32(mloc, lane ^ off));
     nan |= shfl_i32(nan, lane ^ off);
   }
-  __shared__ int nan_sh[kCombineThreads / 64];
   if (lane == 0) {
     red[wave] = mloc;
     nan_sh[wave] = nan;
@@ -470,9 +677,9 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   __syncthreads();
   float M = red[0];
   nan = nan_sh[0];
-  for (int w = 1; w < kCombineThreads / 64; ++w) {
-    M = fmaxf(M, red[w]);
-    nan |= nan_sh[w];
+  for (int wv = 1; wv < kCombineThreads / 64; ++wv) {
+    M = fmaxf(M, red[wv]);
+    nan |= nan_sh[wv];
   }
   __syncthreads();
 
@@ -486,38 +693,42 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
     for (int cc = tid; cc < cnt; cc += kCombineThreads) {
       const float m = ml[(base + cc) * ml_stride];
       const float l = ml[(base + cc) * ml_stride + 1];
-      const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      wsh[cc] = w;
-      lloc += w * l;
+      const float wgt = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      wsh[cc] = wgt;
+      lloc += wgt * l;
     }
     __syncthreads();
 #pragma unroll 8
     for (int cc = 0; cc < cnt; ++cc) {
-      const float w = wsh[cc];
-      if (w != 0.f) {
+      const float wgt = wsh[cc];
+      if (wgt != 0.f) {
         const f32x4_t v = *(const f32x4_t*)(po + (base + cc) * po_stride);
-        acc += w * v;
+        acc += wgt * v;
       }
     }
   }
   for (int off = 32; off > 0; off >>= 1) lloc += shfl_f32(lloc, lane ^ off);
+  __syncthreads();
   if (lane == 0) red[wave] = lloc;
   __syncthreads();
   float Lsum = 0.f;
-  for (int w = 0; w < kCombineThreads / 64; ++w) Lsum += red[w];
+  for (int wv = 0; wv < kCombineThreads / 64; ++wv) Lsum += red[wv];
   const float inv = nan ? NAN : 1.f / Lsum;
   *(f32x4_t*)(a.out + grow * kDl + 4 * tid) = acc * inv;
   if (tid == 0 && a.lse) a.lse[grow] = nan ? NAN : (M + __log2f(Lsum)) * kLn2;
 }
 
+// ===========================================================================
+// Launchers
+// ===========================================================================
 int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (dtype == MLA_DTYPE_BF16)
-    hipLaunchKernelGGL(mla_verify_attn_kernel<false>, dim3((unsigned)grid_blocks),
-                       dim3(KLayout<false>::kThreads), 0, st, a);
+    hipLaunchKernelGGL(mla_verify_attn_bf16_kernel, dim3((unsigned)grid_blocks), dim3(bf16k::kThreads), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL(mla_verify_attn_kernel<true>, dim3((unsigned)grid_blocks),
-                       dim3(KLayout<true>::kThreads), 0, st, a);
+    hipLaunchKernelGGL(mla_verify_attn_f32_kernel, dim3((unsigned)grid_blocks), dim3(f32k::kThreads), 0, st,
+                       a);
   return (int)hipGetLastError();
 }
 

@@ -108,7 +108,8 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
  *   tree_parents device int32 [batch, T]: parent node of each node, -1 = child
  *               of the last prefix token; parent[t] < t.  A node whose parent
  *               chain is invalid gets NaN output rows and lse.
- *   scale       softmax scale applied to the summed dot products
+ *   scale       softmax scale applied to the summed dot products; positive
+ *               and finite (MLA_ERR_INVALID_ARG otherwise)
  *   out         device fp32 [batch*T, H, 512]
  *   lse         device fp32 [batch*T, H] (natural log) or NULL
  *   workspace   device, >= workspace_bytes of the plan, 256-byte aligned.  Holds

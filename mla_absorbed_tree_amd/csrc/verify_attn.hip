@@ -189,40 +189,62 @@ __device__ __forceinline__ float mask_scale_max(float (&sv)[16], const f32x16_t&
 namespace bf16k {
 constexpr int kThreads = 256;
 constexpr int kRows = 128;
-constexpr int kNbuf = 4;                        // LDS ring of key tiles
-constexpr int kAhead = kNbuf - 1;               // tiles in flight ahead of the one in use
+constexpr int kNbuf = 3;                        // LDS ring of key tiles
 constexpr int kCRow = kDl * 2 + 32;             // padded kv_c row: 1056 B
 constexpr int kCBytes = kKeysPerTile * kCRow;   // kv_c part of a tile
 constexpr int kPeRow = kDr * 2;                 // 128 B, 16-byte chunks XOR-swizzled by key
 constexpr int kBufBytes = kCBytes + kKeysPerTile * kPeRow;  // 37888
-constexpr int kPBytes = kRows * kKeysPerTile * 2;           // 8192
-// Page-table entries of upcoming tiles also travel global -> LDS, into a ring
-// of kIdxRing tiles; they are fetched kIdxLead tiles before the keys they name.
+constexpr int kPBytes = kRows * kKeysPerTile * 2;           // 8192 per tile, double-buffered
+// Page-table entries travel global -> LDS too, into a ring of kIdxRing tiles,
+// kIdxLead tiles before the keys they name are fetched.
 constexpr int kIdxRing = 4;
-constexpr int kIdxLead = 3;
+constexpr int kIdxLead = 2;
 constexpr int kIdxBytes = kIdxRing * kKeysPerTile * 4;      // 512
-constexpr int kSmem = kNbuf * kBufBytes + kPBytes + kIdxBytes;
+constexpr int kSmem = kNbuf * kBufBytes + 2 * kPBytes + kIdxBytes;
 // Vector-memory instructions each wave issues per tile: 8 kv_c rows, one
 // block of 8 k_pe rows, one block of 8 page-table entries.
 constexpr int kVmemPerTile = 10;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 }  // namespace bf16k
 
-// One global_load_lds_dword issued by lanes 0..7 of the wave: the page-table
-// entries of this wave's 8 keys of `tile` land in ring slot tile % kIdxRing.
-// Positions past `jmax` (the split's last key) are clamped to it: those keys
-// are loaded but either masked out of the softmax (past the sequence) or
-// never computed (past the split), and their data is a real, finite token.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// The global -> LDS copies below are issued as inline asm so that the
+// compiler's own wait insertion does not treat every later LDS read as
+// dependent on them (which would drain the whole prefetch ring); the kernel
+// waits for them explicitly with wait_vmem<>. Vector-memory loads retire in
+// order, so the compiler's waits for its own loads stay correct.
+
+// global_load_lds_dwordx4 with a scalar base: lane i copies 16 bytes from
+// sbase + voff to LDS byte address lds_base + 16*i.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+// Same with a per-lane 64-bit address.
+__device__ __forceinline__ void lds_dma16_v(const void* src, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"((uint64_t)src)
+               : "memory", "m0");
+}
+
+// Lanes 0..7 fetch the page-table entries of this wave's 8 keys of `tile`
+// into ring slot tile % kIdxRing (one global_load_lds_dword). Positions past
+// `jmax` (the split's last key) are clamped to it: those keys are loaded but
+// either masked out of the softmax (past the sequence) or never computed
+// (past the split), and their data is a real, finite token.
 __device__ __forceinline__ void issue_tile_index(const VerifyArgs& a, char* idx_ring, int kv0, int jmax,
                                                  int tile) {
   using namespace bf16k;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   if (lane < 8) {
     const int j = min(tile * kKeysPerTile + wave * 8 + lane, jmax);
-    const uint32_t base = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(
-            idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8) * 4));
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(base),
+    const uint32_t m0 =
+        __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8) * 4));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0),
                  "v"((uint64_t)(a.kv_indices + kv0 + j))
                  : "memory", "m0");
   }
@@ -236,26 +258,10 @@ __device__ __forceinline__ int tile_slots(const char* idx_ring, int tile) {
   return *(const int*)(idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8 + (lane_id() & 7)) * 4);
 }
 
-// One global_load_lds_dwordx4: lane i copies 16 bytes from its `src` to LDS
-// byte address lds_base + 16*i. Issued as inline asm so that the compiler's
-// own wait insertion does not treat every later LDS read as dependent on it
-// (which would drain the whole prefetch ring); the kernel waits for these
-// loads explicitly with wait_vmem<>. Vector-memory loads retire in order, so
-// the compiler's waits for its own loads stay correct.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"((uint64_t)src)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
 // Enqueue this wave's share of one tile into LDS buffer `buf`: keys 8w..8w+7.
-// Each kv_c row (1 KB) is one 64-lane 16-byte load; the eight 128-byte k_pe
-// rows together are another, lane i fetching chunk (i%8) ^ (i/8) so that the
-// chunks of one key land XOR-swizzled by the key index.
+// Each kv_c row (1 KB) is one 64-lane 16-byte load from a scalar row address;
+// the eight 128-byte k_pe rows together are another, lane i fetching chunk
+// (i%8) ^ (i/8) so that the chunks of one key land XOR-swizzled by the key.
 __device__ __forceinline__ void issue_tile(const VerifyArgs& a, char* buf, int slots) {
   using namespace bf16k;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -264,20 +270,49 @@ __device__ __forceinline__ void issue_tile(const VerifyArgs& a, char* buf, int s
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const int slot = __builtin_amdgcn_readlane(slots, kk);
-    lds_dma16(kvc + (int64_t)slot * a.kv_c_stride + lane * 8, base + (wave * 8 + kk) * kCRow);
+    lds_dma16_s(kvc + (int64_t)slot * a.kv_c_stride, (uint32_t)lane * 16, base + (wave * 8 + kk) * kCRow);
   }
   const int slot = shfl_i32(slots, lane >> 3);
   const int chunk = (lane & 7) ^ (lane >> 3);
-  lds_dma16((const __bf16*)a.k_pe + (int64_t)slot * a.k_pe_stride + chunk * 8,
-            base + kCBytes + wave * 8 * kPeRow);
+  lds_dma16_v((const __bf16*)a.k_pe + (int64_t)slot * a.k_pe_stride + chunk * 8,
+              base + kCBytes + wave * 8 * kPeRow);
+}
+
+// S^T[32 keys x 32 rows] = K . Q^T for this wave's rows from LDS tile `buf`.
+// Batches of four MFMAs with the next batch's LDS reads in flight; the
+// scheduling barriers stop the compiler from hoisting every read at once.
+__device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qreg)[36], int k_off, int kpe_off,
+                                            int kpe_sw, int half) {
+  f32x16_t sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+  bf16x8_t kf[2][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kf[0][j] = *(const bf16x8_t*)(buf + k_off + j * 32);
+#pragma unroll
+  for (int kb = 0; kb < 9; ++kb) {
+    if (kb + 1 < 9) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kc = 4 * (kb + 1) + j;
+        const char* p = kc < 32 ? buf + k_off + kc * 32 : buf + kpe_off + (((2 * (kc - 32) + half) ^ kpe_sw) << 4);
+        kf[(kb + 1) & 1][j] = *(const bf16x8_t*)p;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], qreg[4 * kb + j], sacc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return sacc;
 }
 
 __global__ void __launch_bounds__(bf16k::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   using namespace bf16k;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
-  char* const pbuf = smem + kNbuf * kBufBytes;
-  char* const idx_ring = pbuf + kPBytes;
+  char* const pbuf0 = smem + kNbuf * kBufBytes;
+  char* const idx_ring = pbuf0 + 2 * kPBytes;
 
   BlockWork w;
   if (!map_block(a, w)) return;
@@ -324,6 +359,69 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   f32x16_t oacc[16];  // [f4 * 4 + rb]: feature block 4*wave + f4, row block rb
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
 
+  // Invisible keys of one S^T block get -inf (only tiles that reach the tree
+  // tail or the end of the sequence need this; register i holds key
+  // k0 + (i/4)*8 + 4*half + i%4).
+  auto mask_tile = [&](f32x16_t& sacc, int k0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
+      const bool tail_bit = ((anc >> ((j - w.P) & 63)) & 1ull) != 0;
+      const bool vis = (j < w.P) | ((j < w.N) & tail_bit);
+      sacc[i] = vis ? sacc[i] : -INFINITY;
+    }
+  };
+  // Weights of one (masked) tile for this lane's row, 2^(scale*s*log2e -
+  // m_ref), written as bf16 P^T fragments to P buffer `pb` for every wave.
+  // Split into steps 0..27 so the PV loop can interleave them with its MFMAs;
+  // step k only uses results of earlier steps. The max is taken on raw scores
+  // (scale > 0 keeps the order).
+  struct SoftmaxState {
+    float m[6], mloc, mswap, nmu, psum, p[16];
+    bf16x8_t pk[2];
+  } sm;
+  auto softmax_step = [&](int k, const f32x16_t& sc, char* pb, bool& overflow) {
+    if (k == 0) {
+      sm.m[0] = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+      sm.m[1] = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
+    } else if (k == 1) {
+      sm.m[2] = fmaxf(fmaxf(sc[6], sc[7]), sc[8]);
+      sm.m[3] = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
+    } else if (k == 2) {
+      sm.m[4] = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
+      sm.mloc = fmaxf(fmaxf(fmaxf(sm.m[0], sm.m[1]), sm.m[2]), fmaxf(fmaxf(sm.m[3], sm.m[4]), sc[15]));
+    } else if (k == 3) {
+      sm.mswap = swap_halves(sm.mloc);
+    } else if (k == 6) {
+      const float mx = fmaxf(sm.mloc, sm.mswap) * a.scale_log2;  // row max of the tile, log2 units
+      m_max = fmaxf(m_max, mx);
+      if (m_ref == -INFINITY) m_ref = mx;
+      overflow |= mx > m_ref + kOverflowSlack;
+      sm.nmu = m_ref == -INFINITY ? 0.f : -m_ref;
+      sm.psum = 0.f;
+    } else if (k >= 7 && k < 23) {
+      const int i = k - 7;
+      sm.p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], a.scale_log2, sm.nmu));
+      sm.psum += sm.p[i];
+    } else if (k == 23 || k == 24) {
+      const int u = k - 23;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) sm.pk[u][jj] = (__bf16)sm.p[8 * u + jj];
+    } else if (k == 25 || k == 26) {
+      const int u = k - 25;
+      *(bf16x8_t*)(pb + ((wave * 2 + u) * 64 + lane) * 16) = sm.pk[u];
+    } else if (k == 27) {
+      l_run += sm.psum;
+    }
+  };
+  constexpr int kSoftmaxSteps = 28;
+  auto softmax_to_lds = [&](const f32x16_t& sc, char* pb, bool& overflow) {
+#pragma unroll
+    for (int k = 0; k < kSoftmaxSteps; ++k) softmax_step(k, sc, pb, overflow);
+  };
+  // A tile needs masking when it reaches the tree tail (or the sequence end).
+  auto needs_mask = [&](int k0) { return k0 + kKeysPerTile > w.P; };
+
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int x = 0; x < 16; ++x)
@@ -334,102 +432,86 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 
     if (w.tile_begin < w.tile_end) {
       const int tb = w.tile_begin, te = w.tile_end;
-      // Pipeline: iteration t computes tile t, enqueues the keys of tile
-      // t+kAhead and the page-table entries of tile t+kAhead+kIdxLead. Tiles
-      // past the split repeat its last key (loaded, never computed), which
-      // keeps the number of loads per iteration constant.
       const int jmax = min(w.N, te * kKeysPerTile) - 1;
-#pragma unroll
-      for (int i = 0; i < kAhead; ++i) issue_tile_index(a, idx_ring, w.kv0, jmax, tb + i);
+      // Pipeline. Iteration t: tiles t and t+1 are in LDS, tile t+2 and the
+      // page-table entries of t+2+kIdxLead are fetched; QK and softmax of
+      // tile t+1 run while the PV of tile t (whose weights every wave wrote in
+      // the previous iteration) keeps the matrix cores busy. Tiles past the
+      // split repeat its last key (loaded, never computed), which keeps the
+      // number of loads per iteration constant.
+      issue_tile_index(a, idx_ring, w.kv0, jmax, tb);
+      issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1);
       wait_vmem<0>();
-#pragma unroll
-      for (int i = 0; i < kAhead; ++i) {
-        issue_tile(a, smem + ((tb + i) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + i));
-        issue_tile_index(a, idx_ring, w.kv0, jmax, tb + i + kIdxLead);
+      issue_tile(a, smem + (tb % kNbuf) * kBufBytes, tile_slots(idx_ring, tb));
+      issue_tile_index(a, idx_ring, w.kv0, jmax, tb + kIdxLead);
+      issue_tile(a, smem + ((tb + 1) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + 1));
+      issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1 + kIdxLead);
+      wait_vmem<kVmemPerTile + 1>();  // this wave's part of tile tb
+      block_sync();
+      {
+        f32x16_t s0 = qk_tile(smem + (tb % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half);
+        if (needs_mask(tb * kKeysPerTile)) mask_tile(s0, tb * kKeysPerTile);
+        softmax_to_lds(s0, pbuf0 + (tb & 1) * kPBytes, overflow);
       }
 
       for (int tile = tb; tile < te; ++tile) {
-        // Loads issued after this wave's keys of `tile`: its index block plus
-        // kAhead-1 later iterations. Waiting down to that count also lands the
-        // index block of tile+kAhead (issued kIdxLead iterations ago).
-        static_assert(kIdxLead == kAhead, "wait count below assumes equal leads");
-        wait_vmem<kVmemPerTile * (kAhead - 1)>();
-        block_sync();  // the whole tile is in LDS; every wave has finished tile-1
-        const char* buf = smem + (tile % kNbuf) * kBufBytes;
-        issue_tile(a, smem + ((tile + kAhead) % kNbuf) * kBufBytes, tile_slots(idx_ring, tile + kAhead));
-        issue_tile_index(a, idx_ring, w.kv0, jmax, tile + kAhead + kIdxLead);
-        const int k0 = tile * kKeysPerTile;
-
-        // ---- S^T = K . Q^T (this wave's 32 rows) ---------------------------
-        // Batches of four MFMAs with the next batch's LDS reads in flight; the
-        // scheduling barriers stop the compiler from hoisting every read.
-        f32x16_t sacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        {
-          bf16x8_t kf[2][4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) kf[0][j] = *(const bf16x8_t*)(buf + k_off + j * 32);
-#pragma unroll
-          for (int kb = 0; kb < 9; ++kb) {
-            if (kb + 1 < 9) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int kc = 4 * (kb + 1) + j;
-                const char* p = kc < 32 ? buf + k_off + kc * 32
-                                        : buf + kpe_off + (((2 * (kc - 32) + half) ^ kpe_sw) << 4);
-                kf[(kb + 1) & 1][j] = *(const bf16x8_t*)p;
-              }
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], qreg[4 * kb + j], sacc, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-
-        // ---- mask, scale, weights -----------------------------------------
-        float sv[16];
-        const float mx = mask_scale_max(sv, sacc, a.scale_log2, k0, half, w.P, w.N, anc);
-        m_max = fmaxf(m_max, mx);
-        if (m_ref == -INFINITY) m_ref = mx;
-        overflow |= mx > m_ref + kOverflowSlack;
-        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
-          psum += sv[i];
-        }
-        l_run += psum;
-        // P^T operand fragments of this wave's rows go to LDS for all waves.
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t pk;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) pk[jj] = (__bf16)sv[8 * u + jj];
-          *(bf16x8_t*)(pbuf + ((wave * 2 + u) * 64 + lane) * 16) = pk;
-        }
+        // Loads issued after this wave's keys of tile+1: one index block.
+        // (The index block of tile+2 was issued before them.)
+        wait_vmem<1>();
         wait_lds();
-        block_sync();
+        block_sync();  // P(tile) and tile+1 are visible; every wave has finished PV(tile-1)
+        issue_tile(a, smem + ((tile + 2) % kNbuf) * kBufBytes, tile_slots(idx_ring, tile + 2));
+        issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
 
-        // ---- O^T[this wave's 128 features x 128 rows] += V^T . P^T ---------
+        const char* buf = smem + (tile % kNbuf) * kBufBytes;
+        const char* pb = pbuf0 + (tile & 1) * kPBytes;
+        // Scores of tile+1. On the last tile there is none: all -inf makes the
+        // softmax step below a no-op for the row state.
+        f32x16_t snext;
+        const int k1 = (tile + 1) * kKeysPerTile;
+        if (tile + 1 < te) {
+          snext = qk_tile(smem + ((tile + 1) % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half);
+          if (needs_mask(k1)) mask_tile(snext, k1);
+        } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t pb[4];
+          for (int i = 0; i < 16; ++i) snext[i] = -INFINITY;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- O^T[this wave's 128 features x 128 rows] += V^T . P^T (tile),
+        //      with the weights of tile+1 (VALU) threaded between the MFMAs.
+        // Group g = (u, f4) = (g/4, g%4) issues 4 MFMAs (row blocks); V^T for
+        // group g+1 and P^T for u=1 are read one group ahead.
+        {
+          bf16x8_t pbr[2][4];
+          i16x4_t vf[2][2];
+          auto load_v = [&](int g, i16x4_t (&dst)[2]) {
+            const char* vp = buf + v_off + (16 * (g >> 2)) * kCRow + (g & 3) * 64;
+            dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vp);
+            dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 8 * kCRow));
+          };
+          auto load_p = [&](int u) {
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) pb[rb] = *(const bf16x8_t*)(pbuf + ((rb * 2 + u) * 64 + lane) * 16);
+            for (int rb = 0; rb < 4; ++rb) pbr[u][rb] = *(const bf16x8_t*)(pb + ((rb * 2 + u) * 64 + lane) * 16);
+          };
+          load_p(0);
+          load_v(0, vf[0]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int f4 = 0; f4 < 4; ++f4) {
-            const char* vp = buf + v_off + (16 * u) * kCRow + f4 * 64;
-            const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vp);
-            const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 8 * kCRow));
-            const bf16x8_t vf =
-                __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int g = 0; g < 8; ++g) {
+            if (g + 1 < 8) load_v(g + 1, vf[(g + 1) & 1]);
+            if (g == 2) load_p(1);
+            const bf16x8_t va = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(vf[g & 1][0], vf[g & 1][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-              oacc[f4 * 4 + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[rb], oacc[f4 * 4 + rb], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int rb = 0; rb < 4; ++rb) {
+              const int f4 = g & 3;
+              oacc[f4 * 4 + rb] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbr[g >> 2][rb], oacc[f4 * 4 + rb], 0, 0, 0);
+              const int k = 4 * g + rb;
+              if (k < kSoftmaxSteps) softmax_step(k, snext, pbuf0 + ((tile + 1) & 1) * kPBytes, overflow);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
@@ -443,7 +525,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // Row statistics travel from the QK owner of each row to every wave.
   const float l_tot = l_run + swap_halves(l_run);
   __syncthreads();
-  float2* stats = (float2*)pbuf;
+  float2* stats = (float2*)pbuf0;
   if (half == 0) stats[wave * 32 + qcol] = make_float2(node_ok ? m_ref : NAN, l_tot);
   __syncthreads();
   // Accumulator register i of block (f4, rb) holds feature

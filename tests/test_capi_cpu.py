@@ -102,6 +102,10 @@ def test_run_argument_checks_happen_before_any_launch(B):
     with pytest.raises(B.MlaVerifyError) as e:
         B.mla_verify_run(p, *args, float("nan"), fake, fake, fake, ws, stream=0)
     assert e.value.status == B.MLA_ERR_INVALID_ARG
+    for bad in (0.0, -0.5, float("inf")):
+        with pytest.raises(B.MlaVerifyError) as e:
+            B.mla_verify_run(p, *args, bad, fake, fake, fake, ws, stream=0)
+        assert e.value.status == B.MLA_ERR_INVALID_ARG
     with pytest.raises(B.MlaVerifyError) as e:
         B.mla_verify_tree_masks(fake, 1, 65, fake, stream=0)
     assert e.value.status == B.MLA_ERR_INVALID_ARG

@@ -190,10 +190,14 @@ namespace bf16k {
 constexpr int kThreads = 256;
 constexpr int kRows = 128;
 constexpr int kNbuf = 3;                        // LDS ring of key tiles
-constexpr int kCRow = kDl * 2 + 32;             // padded kv_c row: 1056 B
+// Padded kv_c row: 1168 B = 292 dwords = 36 (mod 64 banks). The 16 keys one
+// QK operand read serves per LDS cycle then start in 16 distinct 4-bank
+// groups (conflict-free); the transpose reads of PV see 2-way conflicts,
+// which no plain padding avoids together with the former.
+constexpr int kCRow = kDl * 2 + 144;
 constexpr int kCBytes = kKeysPerTile * kCRow;   // kv_c part of a tile
 constexpr int kPeRow = kDr * 2;                 // 128 B, 16-byte chunks XOR-swizzled by key
-constexpr int kBufBytes = kCBytes + kKeysPerTile * kPeRow;  // 37888
+constexpr int kBufBytes = kCBytes + kKeysPerTile * kPeRow;  // 41472
 constexpr int kPBytes = kRows * kKeysPerTile * 2;           // 8192 per tile, double-buffered
 // Page-table entries travel global -> LDS too, into a ring of kIdxRing tiles,
 // kIdxLead tiles before the keys they name are fetched.
@@ -217,20 +221,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // waits for them explicitly with wait_vmem<>. Vector-memory loads retire in
 // order, so the compiler's waits for its own loads stay correct.
 
-// global_load_lds_dwordx4 with a scalar base: lane i copies 16 bytes from
-// sbase + voff to LDS byte address lds_base + 16*i.
-__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-// Same with a per-lane 64-bit address.
-__device__ __forceinline__ void lds_dma16_v(const void* src, uint32_t lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"((uint64_t)src)
-               : "memory", "m0");
-}
-
 // Lanes 0..7 fetch the page-table entries of this wave's 8 keys of `tile`
 // into ring slot tile % kIdxRing (one global_load_lds_dword). Positions past
 // `jmax` (the split's last key) are clamped to it: those keys are loaded but
@@ -239,12 +229,12 @@ __device__ __forceinline__ void lds_dma16_v(const void* src, uint32_t lds_base) 
 __device__ __forceinline__ void issue_tile_index(const VerifyArgs& a, char* idx_ring, int kv0, int jmax,
                                                  int tile) {
   using namespace bf16k;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   if (lane < 8) {
     const int j = min(tile * kKeysPerTile + wave * 8 + lane, jmax);
     const uint32_t m0 =
         __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8) * 4));
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0),
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0),
                  "v"((uint64_t)(a.kv_indices + kv0 + j))
                  : "memory", "m0");
   }
@@ -254,35 +244,72 @@ __device__ __forceinline__ void issue_tile_index(const VerifyArgs& a, char* idx_
 // index ring once this wave's load of them has completed.
 __device__ __forceinline__ int tile_slots(const char* idx_ring, int tile) {
   using namespace bf16k;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
   return *(const int*)(idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8 + (lane_id() & 7)) * 4);
 }
 
-// Enqueue this wave's share of one tile into LDS buffer `buf`: keys 8w..8w+7.
-// Each kv_c row (1 KB) is one 64-lane 16-byte load from a scalar row address;
-// the eight 128-byte k_pe rows together are another, lane i fetching chunk
-// (i%8) ^ (i/8) so that the chunks of one key land XOR-swizzled by the key.
-__device__ __forceinline__ void issue_tile(const VerifyArgs& a, char* buf, int slots) {
+// Loads of this wave's share of one tile (keys 8w..8w+7) into an LDS buffer,
+// with every address prepared once so that each load is a couple of
+// instructions: the 64-bit kv_c row addresses sit in lanes 0..7, the k_pe
+// address is per lane. Parts 0..7 are the kv_c rows (1 KB, one 64-lane
+// 16-byte load from a scalar row address each); part 8 is the eight 128-byte
+// k_pe rows together, lane i fetching chunk (i%8) ^ (i/8) so that the chunks of
+// one key land XOR-swizzled by the key index.
+constexpr int kTileParts = 9;
+struct TileLoads {
+  uint32_t row_lo, row_hi;  // lanes 0..7: kv_c row address of key 8w + lane
+  uint64_t kpe;             // per lane: k_pe chunk address
+  uint32_t lds_base;        // wave-uniform: LDS address of this wave's first row
+};
+
+__device__ __forceinline__ TileLoads prepare_tile(const VerifyArgs& a, const char* buf, int slots, int wave) {
   using namespace bf16k;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const __bf16* kvc = (const __bf16*)a.kv_c;
-  const uint32_t base = lds_addr(buf);
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const int slot = __builtin_amdgcn_readlane(slots, kk);
-    lds_dma16_s(kvc + (int64_t)slot * a.kv_c_stride, (uint32_t)lane * 16, base + (wave * 8 + kk) * kCRow);
-  }
-  const int slot = shfl_i32(slots, lane >> 3);
+  const int lane = lane_id();
+  TileLoads t;
+  const uint64_t row = (uint64_t)(uintptr_t)a.kv_c + (uint64_t)(int64_t)slots * (uint64_t)a.kv_c_stride * 2u;
+  t.row_lo = (uint32_t)row;
+  t.row_hi = (uint32_t)(row >> 32);
+  const int kslot = shfl_i32(slots, lane >> 3);
   const int chunk = (lane & 7) ^ (lane >> 3);
-  lds_dma16_v((const __bf16*)a.k_pe + (int64_t)slot * a.k_pe_stride + chunk * 8,
-              base + kCBytes + wave * 8 * kPeRow);
+  t.kpe = (uint64_t)(uintptr_t)a.k_pe + ((uint64_t)(int64_t)kslot * (uint64_t)a.k_pe_stride + chunk * 8) * 2u;
+  t.lds_base = lds_addr(buf) + wave * 8 * kCRow;
+  return t;
+}
+
+__device__ __forceinline__ void issue_tile_part(const TileLoads& t, int wave, int part) {
+  using namespace bf16k;
+  if (part < 8) {
+    // readlane returns int: widen through uint32_t so the low word is not sign-extended.
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)t.row_lo, part);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)t.row_hi, part);
+    const uint64_t row = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const uint32_t m0 = t.lds_base + part * kCRow;
+    // s_nop 4: the scalar base was just written by v_readlane, and a VMEM read
+    // of a VALU-written SGPR needs 5 wait states; it also covers the one wait
+    // state between writing M0 and an LDS-DMA load.
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0),
+                 "v"((uint32_t)lane_id() * 16), "s"(row)
+                 : "memory", "m0");
+  } else {
+    const uint32_t m0 = t.lds_base - wave * 8 * kCRow + kCBytes + wave * 8 * kPeRow;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(t.kpe)
+                 : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ void issue_tile(const VerifyArgs& a, char* buf, int slots, int wave) {
+  const TileLoads t = prepare_tile(a, buf, slots, wave);
+#pragma unroll
+  for (int part = 0; part < kTileParts; ++part) issue_tile_part(t, wave, part);
 }
 
 // S^T[32 keys x 32 rows] = K . Q^T for this wave's rows from LDS tile `buf`.
 // Batches of four MFMAs with the next batch's LDS reads in flight; the
 // scheduling barriers stop the compiler from hoisting every read at once.
+// between(kb) runs after the MFMAs of batch kb (0..8) are issued.
+template <typename Between>
 __device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qreg)[36], int k_off, int kpe_off,
-                                            int kpe_sw, int half) {
+                                            int kpe_sw, int half, Between&& between) {
   f32x16_t sacc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
@@ -302,6 +329,7 @@ __device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qr
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], qreg[4 * kb + j], sacc, 0, 0, 0);
+    between(kb);
     __builtin_amdgcn_sched_barrier(0);
   }
   return sacc;
@@ -319,7 +347,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   const int T = a.tree_nodes, H = a.heads;
 
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;  // uniform: keep it scalar
   const int half = lane >> 5;   // k slice of MFMA operands / key quartet of S^T rows
   const int qcol = lane & 31;   // column of the 32x32 blocks
 
@@ -442,14 +470,14 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb);
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1);
       wait_vmem<0>();
-      issue_tile(a, smem + (tb % kNbuf) * kBufBytes, tile_slots(idx_ring, tb));
+      issue_tile(a, smem + (tb % kNbuf) * kBufBytes, tile_slots(idx_ring, tb), wave);
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb + kIdxLead);
-      issue_tile(a, smem + ((tb + 1) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + 1));
+      issue_tile(a, smem + ((tb + 1) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + 1), wave);
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1 + kIdxLead);
       wait_vmem<kVmemPerTile + 1>();  // this wave's part of tile tb
       block_sync();
       {
-        f32x16_t s0 = qk_tile(smem + (tb % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half);
+        f32x16_t s0 = qk_tile(smem + (tb % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half, [](int) {});
         if (needs_mask(tb * kKeysPerTile)) mask_tile(s0, tb * kKeysPerTile);
         softmax_to_lds(s0, pbuf0 + (tb & 1) * kPBytes, overflow);
       }
@@ -460,7 +488,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         wait_vmem<1>();
         wait_lds();
         block_sync();  // P(tile) and tile+1 are visible; every wave has finished PV(tile-1)
-        issue_tile(a, smem + ((tile + 2) % kNbuf) * kBufBytes, tile_slots(idx_ring, tile + 2));
+        // Tile+2 goes into the buffer tile-1 used.
+        issue_tile(a, smem + ((tile + 2) % kNbuf) * kBufBytes, tile_slots(idx_ring, tile + 2), wave);
         issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
 
         const char* buf = smem + (tile % kNbuf) * kBufBytes;
@@ -470,7 +499,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         f32x16_t snext;
         const int k1 = (tile + 1) * kKeysPerTile;
         if (tile + 1 < te) {
-          snext = qk_tile(smem + ((tile + 1) % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half);
+          snext = qk_tile(smem + ((tile + 1) % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half,
+                          [](int) {});
           if (needs_mask(k1)) mask_tile(snext, k1);
         } else {
 #pragma unroll

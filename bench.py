@@ -122,7 +122,7 @@ def bench_workload(name, steps, warmup, num_splits=None):
         "kernels_ms": {"attention": attn_ms, "combine": comb_ms},
         "plan": mv.info,
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS, "traffic": measured_traffic(name),
                      "kernel": "mla_verify_attn_kernel<bf16>",
                      "flops_per_launch": flops, "avg_launch_ms": attn_ms},
         "config": {"workload": name, "batch": cfg.batch, "heads": cfg.heads,
@@ -135,6 +135,26 @@ def bench_workload(name, steps, warmup, num_splits=None):
     del d
     torch.cuda.empty_cache()
     return res, x
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None when
+    the kernel source changed since they were taken."""
+    import hashlib
+    src = os.path.join(ROOT, "mla_absorbed_tree_amd", "csrc", "verify_attn.hip")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            prof = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if prof.get("kernel_source_sha256") != sha:
+        return None
+    w = prof.get("workloads", {}).get(workload)
+    return None if w is None else float(w["traffic_bytes"])
 
 
 def cpu_baseline(x, budget_s=15.0):

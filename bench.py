@@ -123,7 +123,7 @@ def bench_workload(name, steps, warmup, num_splits=None):
         "plan": mv.info,
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS, "traffic": measured_traffic(name),
-                     "kernel": "mla_verify_attn_kernel<bf16>",
+                     "kernel": "mla_verify_attn_bf16_kernel",
                      "flops_per_launch": flops, "avg_launch_ms": attn_ms},
         "config": {"workload": name, "batch": cfg.batch, "heads": cfg.heads,
                    "prefix": cfg.prefix if cfg.prefix is not None else list(cfg.prefix_range),

@@ -200,9 +200,10 @@ constexpr int kPeRow = kDr * 2;                 // 128 B, 16-byte chunks XOR-swi
 constexpr int kBufBytes = kCBytes + kKeysPerTile * kPeRow;  // 41472
 constexpr int kPBytes = kRows * kKeysPerTile * 2;           // 8192 per tile, double-buffered
 // Page-table entries travel global -> LDS too, into a ring of kIdxRing tiles,
-// kIdxLead tiles before the keys they name are fetched.
+// kIdxLead tiles before the keys they name are fetched; the addresses of a
+// tile's loads are prepared one iteration before the loads are issued.
 constexpr int kIdxRing = 4;
-constexpr int kIdxLead = 2;
+constexpr int kIdxLead = 3;
 constexpr int kIdxBytes = kIdxRing * kKeysPerTile * 4;      // 512
 constexpr int kSmem = kNbuf * kBufBytes + 2 * kPBytes + kIdxBytes;
 // Vector-memory instructions each wave issues per tile: 8 kv_c rows, one
@@ -262,17 +263,25 @@ struct TileLoads {
   uint32_t lds_base;        // wave-uniform: LDS address of this wave's first row
 };
 
-__device__ __forceinline__ TileLoads prepare_tile(const VerifyArgs& a, const char* buf, int slots, int wave) {
+// prepare_tile in three steps (so a loop can spread them between MFMAs):
+// kv_c row addresses, then the lane shuffle for k_pe, then the k_pe address.
+__device__ __forceinline__ void prepare_rows(TileLoads& t, const VerifyArgs& a, const char* buf, int slots, int wave) {
   using namespace bf16k;
-  const int lane = lane_id();
-  TileLoads t;
   const uint64_t row = (uint64_t)(uintptr_t)a.kv_c + (uint64_t)(int64_t)slots * (uint64_t)a.kv_c_stride * 2u;
   t.row_lo = (uint32_t)row;
   t.row_hi = (uint32_t)(row >> 32);
-  const int kslot = shfl_i32(slots, lane >> 3);
+  t.lds_base = lds_addr(buf) + wave * 8 * kCRow;
+}
+__device__ __forceinline__ int prepare_kpe_slot(int slots) { return shfl_i32(slots, lane_id() >> 3); }
+__device__ __forceinline__ void prepare_kpe(TileLoads& t, const VerifyArgs& a, int kslot) {
+  const int lane = lane_id();
   const int chunk = (lane & 7) ^ (lane >> 3);
   t.kpe = (uint64_t)(uintptr_t)a.k_pe + ((uint64_t)(int64_t)kslot * (uint64_t)a.k_pe_stride + chunk * 8) * 2u;
-  t.lds_base = lds_addr(buf) + wave * 8 * kCRow;
+}
+__device__ __forceinline__ TileLoads prepare_tile(const VerifyArgs& a, const char* buf, int slots, int wave) {
+  TileLoads t;
+  prepare_rows(t, a, buf, slots, wave);
+  prepare_kpe(t, a, prepare_kpe_slot(slots));
   return t;
 }
 
@@ -297,8 +306,7 @@ __device__ __forceinline__ void issue_tile_part(const TileLoads& t, int wave, in
   }
 }
 
-__device__ __forceinline__ void issue_tile(const VerifyArgs& a, char* buf, int slots, int wave) {
-  const TileLoads t = prepare_tile(a, buf, slots, wave);
+__device__ __forceinline__ void issue_tile(const TileLoads& t, int wave) {
 #pragma unroll
   for (int part = 0; part < kTileParts; ++part) issue_tile_part(t, wave, part);
 }
@@ -469,11 +477,15 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       // number of loads per iteration constant.
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb);
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1);
+      issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 2);
       wait_vmem<0>();
-      issue_tile(a, smem + (tb % kNbuf) * kBufBytes, tile_slots(idx_ring, tb), wave);
+      issue_tile(prepare_tile(a, smem + (tb % kNbuf) * kBufBytes, tile_slots(idx_ring, tb), wave), wave);
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb + kIdxLead);
-      issue_tile(a, smem + ((tb + 1) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + 1), wave);
+      issue_tile(prepare_tile(a, smem + ((tb + 1) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + 1), wave), wave);
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1 + kIdxLead);
+      // Loads of tile tb+2, issued at the top of the first iteration.
+      TileLoads pending =
+          prepare_tile(a, smem + ((tb + 2) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + 2), wave);
       wait_vmem<kVmemPerTile + 1>();  // this wave's part of tile tb
       block_sync();
       {
@@ -483,14 +495,22 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       }
 
       for (int tile = tb; tile < te; ++tile) {
-        // Loads issued after this wave's keys of tile+1: one index block.
-        // (The index block of tile+2 was issued before them.)
-        wait_vmem<1>();
+        // Everything this wave issued in the previous iteration (the keys of
+        // tile+1 and the index block of tile+4) has landed.
+        wait_vmem<0>();
         wait_lds();
         block_sync();  // P(tile) and tile+1 are visible; every wave has finished PV(tile-1)
-        // Tile+2 goes into the buffer tile-1 used.
-        issue_tile(a, smem + ((tile + 2) % kNbuf) * kBufBytes, tile_slots(idx_ring, tile + 2), wave);
+        // Tile+2 goes into the buffer tile-1 used; its addresses were prepared
+        // during the previous iteration. Four loads go now, five between the
+        // QK batches: a burst of all nine from every wave queues in the
+        // vector-memory path and stalls the issuing waves.
+#pragma unroll
+        for (int part = 0; part < 4; ++part) issue_tile_part(pending, wave, part);
         issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
+        auto late_part = [&](int kb) {
+          if (kb == 1 || kb == 3 || kb == 5 || kb == 7) issue_tile_part(pending, wave, 4 + (kb >> 1));
+          if (kb == 8) issue_tile_part(pending, wave, 8);
+        };
 
         const char* buf = smem + (tile % kNbuf) * kBufBytes;
         const char* pb = pbuf0 + (tile & 1) * kPBytes;
@@ -499,10 +519,11 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         f32x16_t snext;
         const int k1 = (tile + 1) * kKeysPerTile;
         if (tile + 1 < te) {
-          snext = qk_tile(smem + ((tile + 1) % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half,
-                          [](int) {});
+          snext = qk_tile(smem + ((tile + 1) % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half, late_part);
           if (needs_mask(k1)) mask_tile(snext, k1);
         } else {
+#pragma unroll
+          for (int part = 4; part < kTileParts; ++part) issue_tile_part(pending, wave, part);
 #pragma unroll
           for (int i = 0; i < 16; ++i) snext[i] = -INFINITY;
         }
@@ -512,6 +533,16 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         //      with the weights of tile+1 (VALU) threaded between the MFMAs.
         // Group g = (u, f4) = (g/4, g%4) issues 4 MFMAs (row blocks); V^T for
         // group g+1 and P^T for u=1 are read one group ahead.
+        // Addresses of tile+3's loads (entries landed before this iteration's
+        // wait), prepared in steps between the PV MFMAs.
+        int pslots = 0, pkslot = 0;
+        auto prepare_step = [&](int k) {
+          if (k == 0) pslots = tile_slots(idx_ring, tile + 3);
+          else if (k == 10) {
+            prepare_rows(pending, a, smem + ((tile + 3) % kNbuf) * kBufBytes, pslots, wave);
+            pkslot = prepare_kpe_slot(pslots);
+          } else if (k == 20) prepare_kpe(pending, a, pkslot);
+        };
         {
           bf16x8_t pbr[2][4];
           i16x4_t vf[2][2];
@@ -540,6 +571,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
                   __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbr[g >> 2][rb], oacc[f4 * 4 + rb], 0, 0, 0);
               const int k = 4 * g + rb;
               if (k < kSoftmaxSteps) softmax_step(k, snext, pbuf0 + ((tile + 1) & 1) * kPBytes, overflow);
+              prepare_step(k);
               __builtin_amdgcn_sched_barrier(0);
             }
           }

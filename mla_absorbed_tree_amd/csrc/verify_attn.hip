@@ -334,6 +334,9 @@ __device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qr
         kf[(kb + 1) & 1][j] = *(const bf16x8_t*)p;
       }
     }
+    // Keep the reads of batch kb+1 ahead of the MFMAs of batch kb (left to
+    // itself the scheduler sinks them below and reuses the registers).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], qreg[4 * kb + j], sacc, 0, 0, 0);
@@ -507,23 +510,45 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 #pragma unroll
         for (int part = 0; part < 4; ++part) issue_tile_part(pending, wave, part);
         issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
+        const char* buf = smem + (tile % kNbuf) * kBufBytes;
+        const char* pb = pbuf0 + (tile & 1) * kPBytes;
+        // PV operands: P^T fragments [u][rb] and V^T fragments of two groups.
+        // The first ones are read during the last QK batch so that the first
+        // PV MFMA does not wait for them.
+        bf16x8_t pbr[2][4];
+        i16x4_t vf[2][2];
+        auto load_v = [&](int g, i16x4_t (&dst)[2]) {
+          const char* vp = buf + v_off + (16 * (g >> 2)) * kCRow + (g & 3) * 64;
+          dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vp);
+          dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 8 * kCRow));
+        };
+        auto load_p = [&](int u) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) pbr[u][rb] = *(const bf16x8_t*)(pb + ((rb * 2 + u) * 64 + lane) * 16);
+        };
         auto late_part = [&](int kb) {
           if (kb == 1 || kb == 3 || kb == 5 || kb == 7) issue_tile_part(pending, wave, 4 + (kb >> 1));
           if (kb == 8) issue_tile_part(pending, wave, 8);
+          if (kb == 7) {
+            load_p(0);
+            load_v(0, vf[0]);
+          }
         };
-
-        const char* buf = smem + (tile % kNbuf) * kBufBytes;
-        const char* pb = pbuf0 + (tile & 1) * kPBytes;
         // Scores of tile+1. On the last tile there is none: all -inf makes the
         // softmax step below a no-op for the row state.
         f32x16_t snext;
         const int k1 = (tile + 1) * kKeysPerTile;
         if (tile + 1 < te) {
           snext = qk_tile(smem + ((tile + 1) % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half, late_part);
+          // The scores leave the accumulation registers right away (the
+          // softmax works on them in VGPRs).
+          asm volatile("" : "+v"(snext));
           if (needs_mask(k1)) mask_tile(snext, k1);
         } else {
 #pragma unroll
           for (int part = 4; part < kTileParts; ++part) issue_tile_part(pending, wave, part);
+          load_p(0);
+          load_v(0, vf[0]);
 #pragma unroll
           for (int i = 0; i < 16; ++i) snext[i] = -INFINITY;
         }
@@ -544,20 +569,6 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
           } else if (k == 20) prepare_kpe(pending, a, pkslot);
         };
         {
-          bf16x8_t pbr[2][4];
-          i16x4_t vf[2][2];
-          auto load_v = [&](int g, i16x4_t (&dst)[2]) {
-            const char* vp = buf + v_off + (16 * (g >> 2)) * kCRow + (g & 3) * 64;
-            dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vp);
-            dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 8 * kCRow));
-          };
-          auto load_p = [&](int u) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) pbr[u][rb] = *(const bf16x8_t*)(pb + ((rb * 2 + u) * 64 + lane) * 16);
-          };
-          load_p(0);
-          load_v(0, vf[0]);
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int g = 0; g < 8; ++g) {
             if (g + 1 < 8) load_v(g + 1, vf[(g + 1) & 1]);

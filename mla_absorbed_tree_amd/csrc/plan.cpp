@@ -104,6 +104,21 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
       for (int b = 0; b < p.batch; ++b)
         plan.splits[b] = int32_t(std::max<int64_t>(1, (tiles[b] + chunk - 1) / chunk));
     }
+    // Every KV chunk runs on one XCD (its row blocks share that XCD's L2):
+    // with fewer chunks than XCDs some XCDs would idle, so split the longest
+    // sequences further (while chunks stay at least kMinChunkTiles long).
+    for (;;) {
+      int64_t total = 0;
+      for (int b = 0; b < p.batch; ++b) total += plan.splits[b];
+      if (total >= kXcds) break;
+      int best = -1;
+      for (int b = 0; b < p.batch; ++b) {
+        if (tiles[b] / (plan.splits[b] + 1) < kMinChunkTiles) continue;
+        if (best < 0 || tiles[b] * plan.splits[best] > tiles[best] * plan.splits[b]) best = b;
+      }
+      if (best < 0) break;
+      ++plan.splits[best];
+    }
   }
   plan.split_offset.assign(p.batch + 1, 0);
   for (int b = 0; b < p.batch; ++b) {

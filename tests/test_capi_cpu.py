@@ -64,7 +64,7 @@ def test_forced_and_auto_split_schedules(B):
     info = B.mla_verify_plan_get_info(p)
     assert info["total_splits"] == 256 and info["uses_combine"] == 1
     rows = 32 * 64
-    assert info["grid_blocks"] == 256 * (rows // 128)
+    assert info["grid_blocks"] == 256 * (rows // info["rows_per_block"])
     assert ws >= 256 * rows * (512 + 2) * 4
     B.mla_verify_plan_destroy(p)
     # more splits than key tiles are capped at the tile count
@@ -76,6 +76,11 @@ def test_forced_and_auto_split_schedules(B):
     p, ws = B.mla_verify_plan(16, 64, 64, 1, [5000] * 16)
     info = B.mla_verify_plan_get_info(p)
     assert info["total_splits"] == 16 and info["uses_combine"] == 0 and ws == 256
+    B.mla_verify_plan_destroy(p)
+    # ... but at least one chunk per XCD: 4 long sequences get 2 splits each
+    p, ws = B.mla_verify_plan(4, 64, 64, 1, [32832] * 4)
+    info = B.mla_verify_plan_get_info(p)
+    assert info["total_splits"] == 8 and info["uses_combine"] == 1
     B.mla_verify_plan_destroy(p)
     # fp32 uses 32-row blocks
     p, _ = B.mla_verify_plan(1, 16, 8, 0, [264], num_splits=1)

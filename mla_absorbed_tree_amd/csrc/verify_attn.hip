@@ -794,8 +794,9 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
 // ===========================================================================
 // Merge the split partials of one query row (a workgroup of 128 lanes, 4
 // features per lane): M = max m_c, w_c = 2^(m_c - M), L = sum w_c l_c,
-// out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Empty splits (m = -inf) add
-// nothing; a NaN partial (invalid tree) makes the row NaN.
+// out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Empty splits (m = -inf) get
+// weight 0 (their partial is zeros); a NaN partial (invalid tree) makes the
+// row NaN.
 constexpr int kCombineThreads = 128;
 constexpr int kCombineStage = 256;
 
@@ -853,13 +854,12 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
       lloc += wgt * l;
     }
     __syncthreads();
+    // Unconditional loads (an empty split's partial is zeros with weight 0),
+    // so that several are in flight at once.
 #pragma unroll 8
     for (int cc = 0; cc < cnt; ++cc) {
-      const float wgt = wsh[cc];
-      if (wgt != 0.f) {
-        const f32x4_t v = *(const f32x4_t*)(po + (base + cc) * po_stride);
-        acc += wgt * v;
-      }
+      const f32x4_t v = *(const f32x4_t*)(po + (base + cc) * po_stride);
+      acc += wsh[cc] * v;
     }
   }
   for (int off = 32; off > 0; off >>= 1) lloc += shfl_f32(lloc, lane ^ off);

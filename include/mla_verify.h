@@ -128,7 +128,10 @@ mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void
  * The two halves of mla_verify_run, for callers that schedule or time them
  * separately. mla_verify_attend takes exactly the arguments of mla_verify_run
  * and enqueues the attention kernel: sequences with one KV split write out/lse
- * directly, the others leave per-split partials (m, l, O) in the workspace.
+ * directly, the others leave per-split partials in the workspace: (m, l) in
+ * fp32, and the split's output in the problem dtype (fp32 O for fp32 problems;
+ * bf16 O / l for bf16 problems, whose rounding, <= 2^-9 relative per split,
+ * is far below the bf16 tolerance of the result).
  * mla_verify_combine then merges those partials by log-sum-exp into out/lse
  * (it enqueues nothing when the plan has no split sequence). Calling attend and
  * then combine on one stream with the same workspace equals mla_verify_run.

@@ -95,7 +95,7 @@ mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
   a.out = out;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
-  a.part_o = p.combine ? reinterpret_cast<float*>(ws + p.ws_part_o) : nullptr;
+  a.part_o = p.combine ? static_cast<void*>(ws + p.ws_part_o) : nullptr;
   a.part_ml = p.combine ? reinterpret_cast<float*>(ws + p.ws_part_ml) : nullptr;
   a.kv_c_stride = p.kv_c_stride;
   a.k_pe_stride = p.k_pe_stride;
@@ -118,7 +118,7 @@ mla_status launch_attend(const mlav::Plan& p, const mlav::VerifyArgs& a, void* s
 
 mla_status launch_combine(const mlav::Plan& p, const mlav::VerifyArgs& a, void* stream) {
   if (!p.combine) return MLA_OK;
-  const int e = mlav::launch_verify_combine(a, stream);
+  const int e = mlav::launch_verify_combine(a, p.dtype, stream);
   if (e != 0) return fail(MLA_ERR_HIP, "combine launch failed (hipError " + std::to_string(e) + ")");
   return MLA_OK;
 }

@@ -17,7 +17,9 @@ struct VerifyArgs {
   const int32_t* parents;      // [B, T]
   float* out;                  // [B*T, H, 512]
   float* lse;                  // [B*T, H] or nullptr
-  float* part_o;               // [total_splits, rows_per_seq, 512] (split launches only)
+  // Split partials [total_splits, rows_per_seq, 512] (split launches only):
+  // fp32 O for fp32 problems, bf16 O / l for bf16 problems.
+  void* part_o;
   float* part_ml;              // [total_splits, rows_per_seq, 2]  (m in log2 units, l)
   int64_t kv_c_stride;         // elements
   int64_t k_pe_stride;         // elements
@@ -33,7 +35,7 @@ struct VerifyArgs {
 
 // Launchers (defined in the HIP translation unit). Return the launch error.
 int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks, void* stream);
-int launch_verify_combine(const VerifyArgs& a, void* stream);
+int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream);
 int launch_tree_masks(const int32_t* parents, int32_t batch, int32_t tree_nodes, uint64_t* masks,
                       void* stream);
 

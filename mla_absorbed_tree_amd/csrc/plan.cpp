@@ -141,7 +141,8 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
     plan.ws_part_ml = off;
     off = align_up(off + part_rows * 2 * sizeof(float), 256);
     plan.ws_part_o = off;
-    off = align_up(off + part_rows * kDl * sizeof(float), 256);
+    const size_t part_elem = p.dtype == MLA_DTYPE_BF16 ? 2 : sizeof(float);
+    off = align_up(off + part_rows * kDl * part_elem, 256);
   }
   plan.ws_bytes = off;
   return MLA_OK;

@@ -36,7 +36,7 @@ struct Plan {
   // Workspace layout (byte offsets from the workspace start).
   size_t ws_status = 0;         // int32 status flags
   size_t ws_part_ml = 0;        // float2 (m in log2 units, l) per (split, row)
-  size_t ws_part_o = 0;         // float [512] per (split, row)
+  size_t ws_part_o = 0;         // [512] per (split, row): fp32 O, or bf16 O / l for bf16 problems
   size_t ws_bytes = 0;
 };
 

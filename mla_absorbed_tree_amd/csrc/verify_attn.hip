@@ -362,14 +362,18 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   const int half = lane >> 5;   // k slice of MFMA operands / key quartet of S^T rows
   const int qcol = lane & 31;   // column of the 32x32 blocks
 
+  // The page-table entries of the first three tiles go out first, so that
+  // their round trip overlaps the loads of Q and of the tree.
+  const int jmax0 = min(w.N, w.tile_end * kKeysPerTile) - 1;
+  if (w.tile_begin < w.tile_end) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) issue_tile_index(a, idx_ring, w.kv0, jmax0, w.tile_begin + t);
+  }
+
   // ---- QK role: this lane's query row (wave owns rows 32w..32w+31) ---------
   const int r_local = w.rb * kRows + wave * 32 + qcol;
   const int r_eff = min(r_local, a.rows_per_seq - 1);
   const int64_t grow = (int64_t)w.b * a.rows_per_seq + r_eff;
-  const uint64_t tmask = wave_tree_mask(a.parents + (int64_t)w.b * T, T);
-  const uint64_t anc = node_mask(tmask, r_eff / H);
-  const bool node_ok = w.seq_ok && anc != 0;
-
   bf16x8_t qreg[36];
   {
     const __bf16* qn = (const __bf16*)a.q_nope + grow * kDl + half * 8;
@@ -379,6 +383,9 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) qreg[32 + kc] = *(const bf16x8_t*)(qp + kc * 16);
   }
+  const uint64_t tmask = wave_tree_mask(a.parents + (int64_t)w.b * T, T);
+  const uint64_t anc = node_mask(tmask, r_eff / H);
+  const bool node_ok = w.seq_ok && anc != 0;
 
   // Per-lane LDS address pieces.
   // K (A operand of QK): key = qcol, 8 features at 16*kc + 8*half.
@@ -478,9 +485,11 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       // the previous iteration) keeps the matrix cores busy. Tiles past the
       // split repeat its last key (loaded, never computed), which keeps the
       // number of loads per iteration constant.
-      issue_tile_index(a, idx_ring, w.kv0, jmax, tb);
-      issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1);
-      issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 2);
+      if (pass > 0) {  // pass 0 issued these at the start
+        issue_tile_index(a, idx_ring, w.kv0, jmax, tb);
+        issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1);
+        issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 2);
+      }
       wait_vmem<0>();
       issue_tile(prepare_tile(a, smem + (tb % kNbuf) * kBufBytes, tile_slots(idx_ring, tb), wave), wave);
       issue_tile_index(a, idx_ring, w.kv0, jmax, tb + kIdxLead);
@@ -610,30 +619,41 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     const float2 st = stats[rb * 32 + qcol];
     const bool ok = !(st.x != st.x);
     const int64_t g = (int64_t)w.b * a.rows_per_seq + r;
-    float* dst;
-    float mul;
     if (w.S == 1) {
-      dst = a.out + g * kDl;
-      mul = ok ? 1.f / st.y : NAN;
+      float* dst = a.out + g * kDl;
+      const float mul = ok ? 1.f / st.y : NAN;
       if (wave == 0 && half == 0 && a.lse) a.lse[g] = ok ? (st.x + __log2f(st.y)) * kLn2 : NAN;
+#pragma unroll
+      for (int f4 = 0; f4 < 4; ++f4)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          f32x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = oacc[f4 * 4 + rb][4 * gi + e] * mul;
+          *(f32x4_t*)(dst + 32 * (4 * wave + f4) + 8 * gi + 4 * half) = v;
+        }
     } else {
+      // Split partial: (m, l) in fp32 and the split's own normalised output
+      // O / l in bf16 (half the bytes of the largest store and of the combine's
+      // reads; an empty split stores zeros).
       const int64_t prow = (int64_t)w.c * a.rows_per_seq + r;
-      dst = a.part_o + prow * kDl;
-      mul = 1.f;
+      __bf16* dst = (__bf16*)a.part_o + prow * kDl;
+      const float mul = (ok && st.y > 0.f) ? 1.f / st.y : 0.f;
       if (wave == 0 && half == 0) {
         a.part_ml[2 * prow] = st.x;
         a.part_ml[2 * prow + 1] = ok ? st.y : NAN;
       }
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int f4 = 0; f4 < 4; ++f4)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          bf16x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[f4 * 4 + rb][4 * gi + e] * mul);
+          *(bf16x4_t*)(dst + 32 * (4 * wave + f4) + 8 * gi + 4 * half) = v;
+        }
     }
-#pragma unroll
-    for (int f4 = 0; f4 < 4; ++f4)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        f32x4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = oacc[f4 * 4 + rb][4 * gi + e] * mul;
-        *(f32x4_t*)(dst + 32 * (4 * wave + f4) + 8 * gi + 4 * half) = v;
-      }
   }
 }
 
@@ -771,7 +791,7 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
     if (half == 0 && a.lse) a.lse[grow] = node_ok ? (m_ref + __log2f(l_tot)) * kLn2 : NAN;
   } else {
     const int64_t prow = (int64_t)w.c * a.rows_per_seq + r_eff;
-    dst = a.part_o + prow * kDl;
+    dst = (float*)a.part_o + prow * kDl;
     mul = 1.f;
     if (half == 0) {
       a.part_ml[2 * prow] = node_ok ? m_ref : NAN;
@@ -792,85 +812,108 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
 // ===========================================================================
 // Split combine
 // ===========================================================================
-// Merge the split partials of one query row (a workgroup of 128 lanes, 4
-// features per lane): M = max m_c, w_c = 2^(m_c - M), L = sum w_c l_c,
-// out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Empty splits (m = -inf) get
+// Merge the split partials of kCombineRows consecutive query rows of one
+// sequence: M = max m_c, w_c = 2^(m_c - M), L = sum w_c l_c,
+// out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Partials are fp32 O_c (fp32
+// problems) or bf16 O_c / l_c (bf16 problems, weighted by w_c l_c). Each row
+// has 4 groups of 32 lanes (16 features per lane); group g sums the splits
+// c = g (mod 4), and the groups' sums meet in LDS. The rows of a workgroup
+// are adjacent in every split's partial block. Empty splits (m = -inf) get
 // weight 0 (their partial is zeros); a NaN partial (invalid tree) makes the
 // row NaN.
-constexpr int kCombineThreads = 128;
+constexpr int kCombineRows = 2;
+constexpr int kCombineGroups = 4;
+constexpr int kCombineThreads = 32 * kCombineGroups * kCombineRows;
 constexpr int kCombineStage = 256;
 
+template <typename PartT>
 __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(const VerifyArgs a) {
-  __shared__ float wsh[kCombineStage];
-  __shared__ float red[kCombineThreads / 64];
-  __shared__ int nan_sh[kCombineThreads / 64];
-  const int64_t grow = blockIdx.x;
-  const int b = (int)(grow / a.rows_per_seq);
-  const int r = (int)(grow % a.rows_per_seq);
+  constexpr bool kNormalised = sizeof(PartT) == 2;
+  __shared__ float wsh[kCombineRows][kCombineStage];
+  __shared__ float lsh[kCombineRows][kCombineGroups];
+  __shared__ f32x4_t accsh[kCombineRows][kCombineGroups - 1][32][4];
+  const int row_groups = (a.rows_per_seq + kCombineRows - 1) / kCombineRows;
+  const int b = (int)(blockIdx.x / row_groups);
+  const int tid = threadIdx.x;
+  const int j = tid / (32 * kCombineGroups), grp = (tid >> 5) % kCombineGroups, t32 = tid & 31;
+  const int r = (int)(blockIdx.x % row_groups) * kCombineRows + j;
   const int s0 = a.split_offset[b];
   const int S = a.split_offset[b + 1] - s0;
   if (S <= 1) return;
-  const int tid = threadIdx.x;
-  const int lane = lane_id(), wave = tid >> 6;
-  const float* ml = a.part_ml + 2 * ((int64_t)s0 * a.rows_per_seq + r);
+  const bool live = r < a.rows_per_seq;
+  const int rr = live ? r : a.rows_per_seq - 1;
+  const float* ml = a.part_ml + 2 * ((int64_t)s0 * a.rows_per_seq + rr);
   const int64_t ml_stride = 2 * (int64_t)a.rows_per_seq;
 
-  float mloc = -INFINITY;
+  // Row max and NaN flag over the splits (every group computes it).
+  float M = -INFINITY;
   int nan = 0;
-  for (int cc = tid; cc < S; cc += kCombineThreads) {
+  for (int cc = t32; cc < S; cc += 32) {
     const float m = ml[cc * ml_stride];
     nan |= m != m;
-    mloc = fmaxf(mloc, m);
+    M = fmaxf(M, m);
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    mloc = fmaxf(mloc, shfl_f32(mloc, lane ^ off));
-    nan |= shfl_i32(nan, lane ^ off);
+  for (int off = 16; off > 0; off >>= 1) {
+    M = fmaxf(M, shfl_f32(M, lane_id() ^ off));
+    nan |= shfl_i32(nan, lane_id() ^ off);
   }
-  if (lane == 0) {
-    red[wave] = mloc;
-    nan_sh[wave] = nan;
-  }
-  __syncthreads();
-  float M = red[0];
-  nan = nan_sh[0];
-  for (int wv = 1; wv < kCombineThreads / 64; ++wv) {
-    M = fmaxf(M, red[wv]);
-    nan |= nan_sh[wv];
-  }
-  __syncthreads();
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[4] = {};
   float lloc = 0.f;
-  const float* po = a.part_o + ((int64_t)s0 * a.rows_per_seq + r) * kDl + 4 * tid;
+  const PartT* po = (const PartT*)a.part_o + ((int64_t)s0 * a.rows_per_seq + rr) * kDl + 16 * t32;
   const int64_t po_stride = (int64_t)a.rows_per_seq * kDl;
   for (int base = 0; base < S; base += kCombineStage) {
     const int cnt = min(kCombineStage, S - base);
     __syncthreads();
-    for (int cc = tid; cc < cnt; cc += kCombineThreads) {
-      const float m = ml[(base + cc) * ml_stride];
-      const float l = ml[(base + cc) * ml_stride + 1];
-      const float wgt = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      wsh[cc] = wgt;
-      lloc += wgt * l;
+    if (grp == 0) {
+      for (int cc = t32; cc < cnt; cc += 32) {
+        const float m = ml[(base + cc) * ml_stride];
+        const float l = ml[(base + cc) * ml_stride + 1];
+        const float wgt = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        wsh[j][cc] = kNormalised ? wgt * l : wgt;
+        lloc += wgt * l;
+      }
     }
     __syncthreads();
     // Unconditional loads (an empty split's partial is zeros with weight 0),
     // so that several are in flight at once.
-#pragma unroll 8
-    for (int cc = 0; cc < cnt; ++cc) {
-      const f32x4_t v = *(const f32x4_t*)(po + (base + cc) * po_stride);
-      acc += wsh[cc] * v;
+#pragma unroll 4
+    for (int cc = grp; cc < cnt; cc += kCombineGroups) {
+      const float wgt = wsh[j][cc];
+      const PartT* src = po + (base + cc) * po_stride;
+      if constexpr (kNormalised) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bf16x8_t v = *(const bf16x8_t*)(src + 8 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * q][e] += wgt * (float)v[e];
+            acc[2 * q + 1][e] += wgt * (float)v[4 + e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += wgt * *(const f32x4_t*)(src + 4 * q);
+      }
     }
   }
-  for (int off = 32; off > 0; off >>= 1) lloc += shfl_f32(lloc, lane ^ off);
+  if (grp > 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) accsh[j][grp - 1][t32][q] = acc[q];
+  } else {
+    for (int off = 16; off > 0; off >>= 1) lloc += shfl_f32(lloc, lane_id() ^ off);
+  }
   __syncthreads();
-  if (lane == 0) red[wave] = lloc;
-  __syncthreads();
-  float Lsum = 0.f;
-  for (int wv = 0; wv < kCombineThreads / 64; ++wv) Lsum += red[wv];
-  const float inv = nan ? NAN : 1.f / Lsum;
-  *(f32x4_t*)(a.out + grow * kDl + 4 * tid) = acc * inv;
-  if (tid == 0 && a.lse) a.lse[grow] = nan ? NAN : (M + __log2f(Lsum)) * kLn2;
+  if (grp > 0 || !live) return;
+#pragma unroll
+  for (int g = 0; g < kCombineGroups - 1; ++g)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] += accsh[j][g][t32][q];
+  const int64_t grow = (int64_t)b * a.rows_per_seq + r;
+  const float inv = nan ? NAN : 1.f / lloc;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *(f32x4_t*)(a.out + grow * kDl + 16 * t32 + 4 * q) = acc[q] * inv;
+  if (t32 == 0 && a.lse) a.lse[grow] = nan ? NAN : (M + __log2f(lloc)) * kLn2;
 }
 
 // ===========================================================================
@@ -887,10 +930,14 @@ int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks,
   return (int)hipGetLastError();
 }
 
-int launch_verify_combine(const VerifyArgs& a, void* stream) {
-  const int64_t rows = (int64_t)a.batch * a.rows_per_seq;
-  hipLaunchKernelGGL(mla_verify_combine_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0,
-                     (hipStream_t)stream, a);
+int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream) {
+  const int64_t groups = (int64_t)a.batch * ((a.rows_per_seq + kCombineRows - 1) / kCombineRows);
+  if (dtype == MLA_DTYPE_BF16)
+    hipLaunchKernelGGL(mla_verify_combine_kernel<__bf16>, dim3((unsigned)groups), dim3(kCombineThreads), 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(mla_verify_combine_kernel<float>, dim3((unsigned)groups), dim3(kCombineThreads), 0,
+                       (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

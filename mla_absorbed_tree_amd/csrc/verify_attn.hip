@@ -223,7 +223,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // order, so the compiler's waits for its own loads stay correct.
 
 // Lanes 0..7 fetch the page-table entries of this wave's 8 keys of `tile`
-// into ring slot tile % kIdxRing (one global_load_lds_dword). Positions past
+// into ring slot tile % kIdxRing (one global_load_lds_dword; tile >= 0 and
+// kIdxRing is a power of two). Positions past
 // `jmax` (the split's last key) are clamped to it: those keys are loaded but
 // either masked out of the softmax (past the sequence) or never computed
 // (past the split), and their data is a real, finite token.
@@ -234,7 +235,7 @@ __device__ __forceinline__ void issue_tile_index(const VerifyArgs& a, char* idx_
   if (lane < 8) {
     const int j = min(tile * kKeysPerTile + wave * 8 + lane, jmax);
     const uint32_t m0 =
-        __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8) * 4));
+        __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + ((tile & (kIdxRing - 1)) * kKeysPerTile + wave * 8) * 4));
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0),
                  "v"((uint64_t)(a.kv_indices + kv0 + j))
                  : "memory", "m0");
@@ -246,7 +247,7 @@ __device__ __forceinline__ void issue_tile_index(const VerifyArgs& a, char* idx_
 __device__ __forceinline__ int tile_slots(const char* idx_ring, int tile) {
   using namespace bf16k;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
-  return *(const int*)(idx_ring + ((tile % kIdxRing) * kKeysPerTile + wave * 8 + (lane_id() & 7)) * 4);
+  return *(const int*)(idx_ring + ((tile & (kIdxRing - 1)) * kKeysPerTile + wave * 8 + (lane_id() & 7)) * 4);
 }
 
 // Loads of this wave's share of one tile (keys 8w..8w+7) into an LDS buffer,
@@ -265,12 +266,13 @@ struct TileLoads {
 
 // prepare_tile in three steps (so a loop can spread them between MFMAs):
 // kv_c row addresses, then the lane shuffle for k_pe, then the k_pe address.
-__device__ __forceinline__ void prepare_rows(TileLoads& t, const VerifyArgs& a, const char* buf, int slots, int wave) {
+// buf_lds: LDS address of the destination buffer.
+__device__ __forceinline__ void prepare_rows(TileLoads& t, const VerifyArgs& a, uint32_t buf_lds, int slots, int wave) {
   using namespace bf16k;
   const uint64_t row = (uint64_t)(uintptr_t)a.kv_c + (uint64_t)(int64_t)slots * (uint64_t)a.kv_c_stride * 2u;
   t.row_lo = (uint32_t)row;
   t.row_hi = (uint32_t)(row >> 32);
-  t.lds_base = lds_addr(buf) + wave * 8 * kCRow;
+  t.lds_base = buf_lds + wave * 8 * kCRow;
 }
 __device__ __forceinline__ int prepare_kpe_slot(int slots) { return shfl_i32(slots, lane_id() >> 3); }
 __device__ __forceinline__ void prepare_kpe(TileLoads& t, const VerifyArgs& a, int kslot) {
@@ -280,7 +282,7 @@ __device__ __forceinline__ void prepare_kpe(TileLoads& t, const VerifyArgs& a, i
 }
 __device__ __forceinline__ TileLoads prepare_tile(const VerifyArgs& a, const char* buf, int slots, int wave) {
   TileLoads t;
-  prepare_rows(t, a, buf, slots, wave);
+  prepare_rows(t, a, lds_addr(buf), slots, wave);
   prepare_kpe(t, a, prepare_kpe_slot(slots));
   return t;
 }
@@ -506,20 +508,20 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         softmax_to_lds(s0, pbuf0 + (tb & 1) * kPBytes, overflow);
       }
 
+      // Byte offsets of the buffers of tiles t, t+1 and t+2, rotated each
+      // iteration (tile t+3 reuses the buffer of tile t).
+      int bo0 = (tb % kNbuf) * kBufBytes, bo1 = ((tb + 1) % kNbuf) * kBufBytes, bo2 = ((tb + 2) % kNbuf) * kBufBytes;
       for (int tile = tb; tile < te; ++tile) {
         // Everything this wave issued in the previous iteration (the keys of
-        // tile+1 and the index block of tile+4) has landed.
+        // tile+1 and the index block of tile+1+kIdxLead) has landed.
         wait_vmem<0>();
         wait_lds();
         block_sync();  // P(tile) and tile+1 are visible; every wave has finished PV(tile-1)
         // Tile+2 goes into the buffer tile-1 used; its addresses were prepared
-        // during the previous iteration. Four loads go now, five between the
-        // QK batches: a burst of all nine from every wave queues in the
-        // vector-memory path and stalls the issuing waves.
-#pragma unroll
-        for (int part = 0; part < 4; ++part) issue_tile_part(pending, wave, part);
-        issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
-        const char* buf = smem + (tile % kNbuf) * kBufBytes;
+        // during the previous iteration. One load goes after each QK batch (a
+        // burst of all nine from every wave queues in the vector-memory path
+        // and stalls the issuing waves), the page-table block with the first.
+        const char* buf = smem + bo0;
         const char* pb = pbuf0 + (tile & 1) * kPBytes;
         // PV operands: P^T fragments [u][rb] and V^T fragments of two groups.
         // The first ones are read during the last QK batch so that the first
@@ -536,8 +538,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
           for (int rb = 0; rb < 4; ++rb) pbr[u][rb] = *(const bf16x8_t*)(pb + ((rb * 2 + u) * 64 + lane) * 16);
         };
         auto late_part = [&](int kb) {
-          if (kb == 1 || kb == 3 || kb == 5 || kb == 7) issue_tile_part(pending, wave, 4 + (kb >> 1));
-          if (kb == 8) issue_tile_part(pending, wave, 8);
+          issue_tile_part(pending, wave, kb);
+          if (kb == 0) issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
           if (kb == 7) {
             load_p(0);
             load_v(0, vf[0]);
@@ -548,14 +550,14 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         f32x16_t snext;
         const int k1 = (tile + 1) * kKeysPerTile;
         if (tile + 1 < te) {
-          snext = qk_tile(smem + ((tile + 1) % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half, late_part);
+          snext = qk_tile(smem + bo1, qreg, k_off, kpe_off, kpe_sw, half, late_part);
           // The scores leave the accumulation registers right away (the
           // softmax works on them in VGPRs).
           asm volatile("" : "+v"(snext));
           if (needs_mask(k1)) mask_tile(snext, k1);
         } else {
-#pragma unroll
-          for (int part = 4; part < kTileParts; ++part) issue_tile_part(pending, wave, part);
+          issue_tile(pending, wave);
+          issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
           load_p(0);
           load_v(0, vf[0]);
 #pragma unroll
@@ -573,7 +575,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         auto prepare_step = [&](int k) {
           if (k == 0) pslots = tile_slots(idx_ring, tile + 3);
           else if (k == 10) {
-            prepare_rows(pending, a, smem + ((tile + 3) % kNbuf) * kBufBytes, pslots, wave);
+            prepare_rows(pending, a, lds_addr(smem) + (uint32_t)bo0, pslots, wave);
             pkslot = prepare_kpe_slot(pslots);
           } else if (k == 20) prepare_kpe(pending, a, pkslot);
         };
@@ -596,6 +598,10 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
             }
           }
         }
+        const int bt = bo0;
+        bo0 = bo1;
+        bo1 = bo2;
+        bo2 = bt;
       }
       wait_vmem<0>();
     }

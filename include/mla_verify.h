@@ -77,6 +77,7 @@ typedef struct {
   int32_t keys_per_tile;    /* keys staged in LDS per step */
   int32_t grid_blocks;      /* workgroups of the attention launch */
   int32_t uses_combine;     /* 1 when a split-combine launch follows */
+  int32_t splits_per_workgroup; /* consecutive splits one workgroup runs (row block fixed) */
   size_t workspace_bytes;   /* same value mla_verify_plan() returned */
 } mla_verify_plan_info;
 
@@ -129,9 +130,10 @@ mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void
  * separately. mla_verify_attend takes exactly the arguments of mla_verify_run
  * and enqueues the attention kernel: sequences with one KV split write out/lse
  * directly, the others leave per-split partials in the workspace: (m, l) in
- * fp32, and the split's output in the problem dtype (fp32 O for fp32 problems;
- * bf16 O / l for bf16 problems, whose rounding, <= 2^-9 relative per split,
- * is far below the bf16 tolerance of the result).
+ * fp32, and the split's unnormalised output O = l * o_split in the problem
+ * dtype (fp32 for fp32 problems; bf16 for bf16 problems, whose rounding,
+ * <= 2^-9 relative per element, moves the result by <= 2^-9 max |o_split|,
+ * far below the bf16 tolerance).
  * mla_verify_combine then merges those partials by log-sum-exp into out/lse
  * (it enqueues nothing when the plan has no split sequence). Calling attend and
  * then combine on one stream with the same workspace equals mla_verify_run.

@@ -50,7 +50,7 @@ class mla_verify_plan_info(ctypes.Structure):
     _fields_ = [("total_splits", ctypes.c_int32), ("max_splits", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("keys_per_tile", ctypes.c_int32),
                 ("grid_blocks", ctypes.c_int32), ("uses_combine", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("splits_per_workgroup", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
 
 def _load():

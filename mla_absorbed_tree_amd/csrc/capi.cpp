@@ -55,6 +55,7 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
   info->keys_per_tile = mlav::kKeysPerTile;
   info->grid_blocks = int32_t(p.grid_blocks);
   info->uses_combine = p.combine ? 1 : 0;
+  info->splits_per_workgroup = p.group;
   info->workspace_bytes = p.ws_bytes;
   return MLA_OK;
 }
@@ -104,9 +105,12 @@ mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
   a.heads = p.heads;
   a.tree_nodes = p.tree_nodes;
   a.rows_per_seq = p.rows_per_seq;
+  a.part_rows = p.row_blocks * p.rows_per_block;
   a.row_blocks = p.row_blocks;
   a.total_splits = p.total_splits;
   for (int b = 0; b <= p.batch; ++b) a.split_offset[b] = p.split_offset[b];
+  a.group = p.group;
+  for (int b = 0; b <= p.batch; ++b) a.group_offset[b] = p.group_offset[b];
   return MLA_OK;
 }
 

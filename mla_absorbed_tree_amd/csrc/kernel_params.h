@@ -17,10 +17,11 @@ struct VerifyArgs {
   const int32_t* parents;      // [B, T]
   float* out;                  // [B*T, H, 512]
   float* lse;                  // [B*T, H] or nullptr
-  // Split partials [total_splits, rows_per_seq, 512] (split launches only):
-  // fp32 O for fp32 problems, bf16 O / l for bf16 problems.
+  // Split partials [total_splits, part_rows, 512] (split launches only):
+  // unnormalised O = sum of 2^(s - m) v, fp32 for fp32 problems, bf16 for
+  // bf16 problems. Rows past rows_per_seq are padding (never read).
   void* part_o;
-  float* part_ml;              // [total_splits, rows_per_seq, 2]  (m in log2 units, l)
+  float* part_ml;              // [total_splits, part_rows, 2]  (m in log2 units, l)
   int64_t kv_c_stride;         // elements
   int64_t k_pe_stride;         // elements
   float scale_log2;            // softmax scale * log2(e)
@@ -28,9 +29,12 @@ struct VerifyArgs {
   int32_t heads;
   int32_t tree_nodes;
   int32_t rows_per_seq;        // T * H
+  int32_t part_rows;           // row_blocks * rows per workgroup (>= rows_per_seq)
   int32_t row_blocks;          // workgroups along the rows of one sequence
   int32_t total_splits;
   int32_t split_offset[MLA_VERIFY_MAX_BATCH + 1];  // first global split of sequence b
+  int32_t group;                                   // consecutive splits per workgroup
+  int32_t group_offset[MLA_VERIFY_MAX_BATCH + 1];  // first split group of sequence b
 };
 
 // Launchers (defined in the HIP translation unit). Return the launch error.

@@ -127,7 +127,20 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
     if (plan.splits[b] > 1) plan.combine = true;
   }
   plan.total_splits = plan.split_offset[p.batch];
-  plan.chunk_groups = (plan.total_splits + kXcds - 1) / kXcds;
+  // Many short splits (a forced split count) would make thousands of
+  // workgroups that each pay the fixed start-up and tail; instead one
+  // workgroup runs several consecutive splits, aiming at about one workgroup
+  // per compute unit. The bf16 kernel only (the fp32 kernel runs one split).
+  plan.group = 1;
+  if (p.dtype == MLA_DTYPE_BF16)
+    plan.group = int32_t(std::max<int64_t>(
+        1, int64_t(plan.total_splits) * plan.row_blocks / kComputeUnits));
+  plan.group = std::min(plan.group, std::max(1, plan.max_splits));
+  plan.group_offset.assign(p.batch + 1, 0);
+  for (int b = 0; b < p.batch; ++b)
+    plan.group_offset[b + 1] = plan.group_offset[b] + (plan.splits[b] + plan.group - 1) / plan.group;
+  plan.total_groups = plan.group_offset[p.batch];
+  plan.chunk_groups = (plan.total_groups + kXcds - 1) / kXcds;
   plan.grid_blocks = int64_t(plan.chunk_groups) * kXcds * plan.row_blocks;
   if (plan.grid_blocks > (int64_t(1) << 31) - 1) {
     err = "launch grid too large";
@@ -137,7 +150,9 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   size_t off = 256;  // status flags live in the first 256 bytes
   plan.ws_status = 0;
   if (plan.combine) {
-    const size_t part_rows = size_t(plan.total_splits) * size_t(plan.rows_per_seq);
+    // Partial rows per split padded to whole row blocks (the bf16 kernel
+    // stores unconditionally, padding rows included).
+    const size_t part_rows = size_t(plan.total_splits) * size_t(plan.row_blocks) * size_t(plan.rows_per_block);
     plan.ws_part_ml = off;
     off = align_up(off + part_rows * 2 * sizeof(float), 256);
     plan.ws_part_o = off;

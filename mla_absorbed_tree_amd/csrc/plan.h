@@ -30,13 +30,19 @@ struct Plan {
   std::vector<int32_t> splits;  // S_b
   std::vector<int32_t> split_offset;  // [batch + 1] prefix sums of S_b
   int32_t total_splits = 0, max_splits = 0;
-  int32_t chunk_groups = 0;     // ceil(total_splits / kXcds)
+  // A workgroup runs `group` consecutive splits of one sequence for one row
+  // block (one stream of key tiles, a partial written at each split end).
+  int32_t group = 1;
+  std::vector<int32_t> group_offset;  // [batch + 1] prefix sums of ceil(S_b / group)
+  int32_t total_groups = 0;
+  int32_t chunk_groups = 0;     // ceil(total_groups / kXcds)
   int64_t grid_blocks = 0;      // attention launch
   bool combine = false;         // some sequence has S_b > 1
   // Workspace layout (byte offsets from the workspace start).
   size_t ws_status = 0;         // int32 status flags
-  size_t ws_part_ml = 0;        // float2 (m in log2 units, l) per (split, row)
-  size_t ws_part_o = 0;         // [512] per (split, row): fp32 O, or bf16 O / l for bf16 problems
+  // Per (split, row), rows padded to row_blocks * rows_per_block per split:
+  size_t ws_part_ml = 0;        // float2 (m in log2 units, l)
+  size_t ws_part_o = 0;         // [512] unnormalised O: fp32, or bf16 for bf16 problems
   size_t ws_bytes = 0;
 };
 

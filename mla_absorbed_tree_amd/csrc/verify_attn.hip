@@ -43,6 +43,12 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
+}
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -127,40 +133,50 @@ __global__ void __launch_bounds__(64) mla_tree_masks_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup -> (sequence, KV split, row block), XCD-aware.
-// Consecutive workgroup ids are dealt to different XCDs; every row block of
-// one KV chunk gets the same XCD so the chunk streams through a single L2.
+// Workgroup -> (sequence, group of consecutive KV splits, row block),
+// XCD-aware. Consecutive workgroup ids are dealt to different XCDs; every row
+// block of one split group gets the same XCD so its keys stream through a
+// single L2. A workgroup runs the splits of its group one after the other as
+// one stream of key tiles (the splits of a sequence are adjacent), writing a
+// partial result at the end of each.
 // ---------------------------------------------------------------------------
 struct BlockWork {
-  int b, s, S, c, rb;
-  int kv0, N, P;
-  int tile_begin, tile_end;
+  int b, S, rb;
+  int s, c;                   // current split: index within the sequence, global index
+  int s_last;                 // one past the group's last split (within the sequence)
+  int kv0, N, P, ntiles;
+  int tile_begin, tile_end;   // key tiles of the whole group
   bool seq_ok;
 };
+
+// First key tile of split s of a sequence with ntiles tiles and S splits.
+__device__ __forceinline__ int split_tile(int s, int ntiles, int S) { return (int)(((int64_t)s * ntiles) / S); }
 
 __device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w) {
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int local = bid / kXcds;
   w.rb = local % a.row_blocks;
-  w.c = (local / a.row_blocks) * kXcds + xcd;
-  if (w.c >= a.total_splits) return false;
+  const int cg = (local / a.row_blocks) * kXcds + xcd;
+  if (cg >= a.group_offset[a.batch]) return false;
   int lo = 0, hi = a.batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (a.split_offset[mid] <= w.c) lo = mid;
+    if (a.group_offset[mid] <= cg) lo = mid;
     else hi = mid - 1;
   }
   w.b = lo;
   w.S = a.split_offset[w.b + 1] - a.split_offset[w.b];
-  w.s = w.c - a.split_offset[w.b];
+  w.s = (cg - a.group_offset[w.b]) * a.group;
+  w.s_last = min(w.s + a.group, w.S);
+  w.c = a.split_offset[w.b] + w.s;
   w.kv0 = a.kv_indptr[w.b];
   w.N = a.kv_indptr[w.b + 1] - w.kv0;
   w.P = w.N - a.tree_nodes;
   w.seq_ok = w.P >= 0;
-  const int ntiles = w.seq_ok ? (w.N + kKeysPerTile - 1) / kKeysPerTile : 0;
-  w.tile_begin = (int)(((int64_t)w.s * ntiles) / w.S);
-  w.tile_end = (int)(((int64_t)(w.s + 1) * ntiles) / w.S);
+  w.ntiles = w.seq_ok ? (w.N + kKeysPerTile - 1) / kKeysPerTile : 0;
+  w.tile_begin = split_tile(w.s, w.ntiles, w.S);
+  w.tile_end = split_tile(w.s_last, w.ntiles, w.S);
   return true;
 }
 
@@ -205,7 +221,14 @@ constexpr int kPBytes = kRows * kKeysPerTile * 2;           // 8192 per tile, do
 constexpr int kIdxRing = 4;
 constexpr int kIdxLead = 3;
 constexpr int kIdxBytes = kIdxRing * kKeysPerTile * 4;      // 512
-constexpr int kSmem = kNbuf * kBufBytes + 2 * kPBytes + kIdxBytes;
+constexpr int kAncBytes = kRows * 8;                          // ancestor mask of each row
+// The rope part of Q (64 features of each row) as each lane's four MFMA
+// operand fragments, [wave][fragment][lane] x 16 bytes.
+constexpr int kQpeBytes = kRows * kDr * 2;                     // 16384
+constexpr int kSmem = kNbuf * kBufBytes + 2 * kPBytes + kIdxBytes + kAncBytes + kQpeBytes;
+// Vector-memory stores one wave issues for a split partial: (m, l) plus
+// 4 row blocks x 4 feature blocks x 2 16-byte pieces.
+constexpr int kPartialStores = 1 + 4 * 4 * 2;
 // Vector-memory instructions each wave issues per tile: 8 kv_c rows, one
 // block of 8 k_pe rows, one block of 8 page-table entries.
 constexpr int kVmemPerTile = 10;
@@ -314,34 +337,36 @@ __device__ __forceinline__ void issue_tile(const TileLoads& t, int wave) {
 }
 
 // S^T[32 keys x 32 rows] = K . Q^T for this wave's rows from LDS tile `buf`.
-// Batches of four MFMAs with the next batch's LDS reads in flight; the
-// scheduling barriers stop the compiler from hoisting every read at once.
-// between(kb) runs after the MFMAs of batch kb (0..8) are issued.
+// Batch 0 is the rope part (both operands from LDS: Q's rope fragments live
+// there, at `qpe` for this lane, to spare 16 registers); batches 1..8 take
+// the latent part of Q from registers. Each batch's LDS reads are issued
+// during the previous batch; the scheduling barriers stop the compiler from
+// hoisting every read at once. between(kb) runs after the MFMAs of batch kb.
 template <typename Between>
-__device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qreg)[36], int k_off, int kpe_off,
-                                            int kpe_sw, int half, Between&& between) {
+__device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qreg)[32], const char* qpe, int k_off,
+                                            int kpe_off, int kpe_sw, int half, Between&& between) {
   f32x16_t sacc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-  bf16x8_t kf[2][4];
+  bf16x8_t kf[2][4], qf[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kf[0][j] = *(const bf16x8_t*)(buf + k_off + j * 32);
+  for (int j = 0; j < 4; ++j) {
+    kf[0][j] = *(const bf16x8_t*)(buf + kpe_off + (((2 * j + half) ^ kpe_sw) << 4));
+    qf[j] = *(const bf16x8_t*)(qpe + j * 64 * 16);
+  }
 #pragma unroll
   for (int kb = 0; kb < 9; ++kb) {
     if (kb + 1 < 9) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kc = 4 * (kb + 1) + j;
-        const char* p = kc < 32 ? buf + k_off + kc * 32 : buf + kpe_off + (((2 * (kc - 32) + half) ^ kpe_sw) << 4);
-        kf[(kb + 1) & 1][j] = *(const bf16x8_t*)p;
-      }
+      for (int j = 0; j < 4; ++j) kf[(kb + 1) & 1][j] = *(const bf16x8_t*)(buf + k_off + (4 * kb + j) * 32);
     }
     // Keep the reads of batch kb+1 ahead of the MFMAs of batch kb (left to
     // itself the scheduler sinks them below and reuses the registers).
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], qreg[4 * kb + j], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], kb == 0 ? qf[j] : qreg[4 * (kb - 1) + j], sacc,
+                                                     0, 0, 0);
     between(kb);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -354,6 +379,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   char* const pbuf0 = smem + kNbuf * kBufBytes;
   char* const idx_ring = pbuf0 + 2 * kPBytes;
+  uint64_t* const anc_lds = (uint64_t*)(idx_ring + kIdxBytes);
+  char* const qpe_lds = idx_ring + kIdxBytes + kAncBytes;
 
   BlockWork w;
   if (!map_block(a, w)) return;
@@ -376,18 +403,33 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   const int r_local = w.rb * kRows + wave * 32 + qcol;
   const int r_eff = min(r_local, a.rows_per_seq - 1);
   const int64_t grow = (int64_t)w.b * a.rows_per_seq + r_eff;
-  bf16x8_t qreg[36];
+  bf16x8_t qreg[32];
+  const char* const qpe_lane = qpe_lds + (wave * 4 * 64 + lane) * 16;
   {
     const __bf16* qn = (const __bf16*)a.q_nope + grow * kDl + half * 8;
     const __bf16* qp = (const __bf16*)a.q_pe + grow * kDr + half * 8;
 #pragma unroll
     for (int kc = 0; kc < 32; ++kc) qreg[kc] = *(const bf16x8_t*)(qn + kc * 16);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) qreg[32 + kc] = *(const bf16x8_t*)(qp + kc * 16);
+    for (int kc = 0; kc < 4; ++kc)  // only this lane reads these back
+      *(bf16x8_t*)(qpe_lane + kc * 64 * 16) = *(const bf16x8_t*)(qp + kc * 16);
   }
   const uint64_t tmask = wave_tree_mask(a.parents + (int64_t)w.b * T, T);
-  const uint64_t anc = node_mask(tmask, r_eff / H);
-  const bool node_ok = w.seq_ok && anc != 0;
+  // This lane's ancestor mask waits in LDS (read by the few tiles that reach
+  // the tree tail and by the epilogue) instead of holding two registers
+  // through the tile loop. Only the QK owner (half 0) writes it; the first
+  // barrier of the pipeline orders the write before every read.
+  {
+    const uint64_t anc = node_mask(tmask, r_eff / H);
+    if (half == 0) anc_lds[wave * 32 + qcol] = w.seq_ok ? anc : 0ull;
+  }
+  // Ancestor mask of this lane's row (0: no valid node), loaded afresh so that
+  // the value is not carried through the loop in registers.
+  auto row_anc = [&]() {
+    int i = wave * 32 + qcol;
+    asm volatile("" : "+v"(i));
+    return anc_lds[i];
+  };
 
   // Per-lane LDS address pieces.
   // K (A operand of QK): key = qcol, 8 features at 16*kc + 8*half.
@@ -406,11 +448,17 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // more than kOverflowSlack the block repeats the split with the exact max.
   f32x16_t oacc[16];  // [f4 * 4 + rb]: feature block 4*wave + f4, row block rb
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
+  // Split boundaries inside the group: the weight sum of a tile that starts
+  // the next split stays out of l_run (it is still in sm.psum when the split
+  // ends, and starts the next split's sum).
+  bool next_starts_split = false;
+  const int s_first = w.s, c_first = w.c;
 
   // Invisible keys of one S^T block get -inf (only tiles that reach the tree
   // tail or the end of the sequence need this; register i holds key
   // k0 + (i/4)*8 + 4*half + i%4).
   auto mask_tile = [&](f32x16_t& sacc, int k0) {
+    const uint64_t anc = row_anc();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
@@ -459,7 +507,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       const int u = k - 25;
       *(bf16x8_t*)(pb + ((wave * 2 + u) * 64 + lane) * 16) = sm.pk[u];
     } else if (k == 27) {
-      l_run += sm.psum;
+      if (!next_starts_split) l_run += sm.psum;
     }
   };
   constexpr int kSoftmaxSteps = 28;
@@ -470,12 +518,102 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // A tile needs masking when it reaches the tree tail (or the sequence end).
   auto needs_mask = [&](int k0) { return k0 + kKeysPerTile > w.P; };
 
+  // Partial of global split c (sequences with several splits): (m, l) from the QK
+  // owner lanes of each row, and this wave's raw O^T blocks in bf16 (half the
+  // bytes of fp32; the rounding is relative to each partial and averages out
+  // in the merge). No exchange between waves, so no barrier.
+  // Accumulator register i of block (f4, rb) holds feature
+  // 32*(4*wave + f4) + (i/4)*8 + 4*half + i%4 of row 32*rb + qcol.
+  // Values 4*gi .. 4*gi+3 of an accumulator block, read out of the
+  // accumulation registers one at a time (left to itself the compiler moves
+  // whole 16-register blocks to VGPRs, which do not fit next to Q).
+  auto read_acc4 = [](const f32x16_t& acc, int gi) {
+    float t0, t1, t2, t3;
+    asm volatile(
+        "v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\t"
+        "v_accvgpr_read_b32 %2, %6\n\tv_accvgpr_read_b32 %3, %7"
+        : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+        : "a"(acc[4 * gi]), "a"(acc[4 * gi + 1]), "a"(acc[4 * gi + 2]), "a"(acc[4 * gi + 3]));
+    return f32x4_t{t0, t1, t2, t3};
+  };
+  //
+  // The partial arrays have a.part_rows (a multiple of kRows) rows per split,
+  // so the rows past rows_per_seq of the last row block have room and every
+  // store below is unconditional: exactly kPartialStores vector-memory
+  // instructions, which the wait after a split boundary relies on.
+  auto emit_partial = [&](int c) {
+    // Lane indices taken afresh (an opaque copy), so that no address below is
+    // computed ahead of the tile loop and kept live through it.
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
+    const int qcol = lq & 31, half = lq >> 5;
+    const float l_tot = l_run + swap_halves(l_run);
+    const bool node_ok = row_anc() != 0;
+    // (m, l) of the row; both lanes of a row hold the same values.
+    const int64_t prow = (int64_t)c * a.part_rows + w.rb * kRows + wave * 32 + qcol;
+    *(float2*)(a.part_ml + 2 * prow) = make_float2(node_ok ? m_ref : NAN, node_ok ? l_tot : NAN);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = w.rb * kRows + rb * 32 + qcol;
+      __bf16* dst = (__bf16*)a.part_o + ((int64_t)c * a.part_rows + r) * kDl + 8 * half;
+#pragma unroll
+      for (int f4 = 0; f4 < 4; ++f4)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          // Values 2m and 2m+1 (features 16m + 4*half + 0..3 and 16m + 8 +
+          // 4*half + 0..3) become 8 consecutive features per lane by one
+          // exchange between the wave halves: the lower half keeps 16m..16m+7,
+          // the upper half gets 16m+8..16m+15.
+          const f32x4_t t0 = read_acc4(oacc[f4 * 4 + rb], 2 * m);
+          const f32x4_t t1 = read_acc4(oacc[f4 * 4 + rb], 2 * m + 1);
+          uint32_t x[2], y[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            x[e] = pack_bf16x2(t0[2 * e], t0[2 * e + 1]);
+            y[e] = pack_bf16x2(t1[2 * e], t1[2 * e + 1]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+            x[e] = sw[0];
+            y[e] = sw[1];
+          }
+          *(u32x4_t*)(dst + 32 * (4 * wave + f4) + 16 * m) = u32x4_t{x[0], x[1], y[0], y[1]};
+          // One pair at a time: otherwise the scheduler reads every
+          // accumulator out at once and runs out of registers.
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  };
+  // Output of a sequence with one split: O / l and lse; each row's
+  // statistics travel from its QK owner to every wave through LDS.
+  auto emit_final = [&]() {
+    const float l_tot = l_run + swap_halves(l_run);
+    float2* stats = (float2*)pbuf0;  // the P buffers are free after the loop
+    const bool node_ok = row_anc() != 0;
+    __syncthreads();
+    if (half == 0) stats[wave * 32 + qcol] = make_float2(node_ok ? m_ref : NAN, l_tot);
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = w.rb * kRows + rb * 32 + qcol;
+      if (r >= a.rows_per_seq) continue;
+      const float2 st = stats[rb * 32 + qcol];
+      const bool ok = !(st.x != st.x);
+      const int64_t g = (int64_t)w.b * a.rows_per_seq + r;
+      float* dst = a.out + g * kDl;
+      const float mul = ok ? 1.f / st.y : NAN;
+      if (wave == 0 && half == 0 && a.lse) a.lse[g] = ok ? (st.x + __log2f(st.y)) * kLn2 : NAN;
+#pragma unroll
+      for (int f4 = 0; f4 < 4; ++f4)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const f32x4_t v = read_acc4(oacc[f4 * 4 + rb], gi);
+          *(f32x4_t*)(dst + 32 * (4 * wave + f4) + 8 * gi + 4 * half) = v * mul;
+        }
+    }
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int x = 0; x < 16; ++x)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
     l_run = 0.f;
+    next_starts_split = false;
     bool overflow = false;
 
     if (w.tile_begin < w.tile_end) {
@@ -503,7 +641,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       wait_vmem<kVmemPerTile + 1>();  // this wave's part of tile tb
       block_sync();
       {
-        f32x16_t s0 = qk_tile(smem + (tb % kNbuf) * kBufBytes, qreg, k_off, kpe_off, kpe_sw, half, [](int) {});
+        f32x16_t s0 = qk_tile(smem + (tb % kNbuf) * kBufBytes, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half, [](int) {});
         if (needs_mask(tb * kKeysPerTile)) mask_tile(s0, tb * kKeysPerTile);
         softmax_to_lds(s0, pbuf0 + (tb & 1) * kPBytes, overflow);
       }
@@ -511,10 +649,23 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       // Byte offsets of the buffers of tiles t, t+1 and t+2, rotated each
       // iteration (tile t+3 reuses the buffer of tile t).
       int bo0 = (tb % kNbuf) * kBufBytes, bo1 = ((tb + 1) % kNbuf) * kBufBytes, bo2 = ((tb + 2) % kNbuf) * kBufBytes;
-      for (int tile = tb; tile < te; ++tile) {
+      int tile = tb;
+      // The splits of the group (at least one), one after the other; the
+      // tile pipeline runs on across their boundaries.
+      int sp = s_first;
+      do {
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
+      const int split_begin = tile, split_end = split_tile(sp + 1, w.ntiles, w.S);
+      for (; tile < split_end; ++tile) {
         // Everything this wave issued in the previous iteration (the keys of
-        // tile+1 and the index block of tile+1+kIdxLead) has landed.
-        wait_vmem<0>();
+        // tile+1 and the index block of tile+1+kIdxLead) has landed. After a
+        // split boundary the partial's stores, issued after those loads, may
+        // still be on their way.
+        if (tile == split_begin && sp != s_first) wait_vmem<kPartialStores>();
+        else wait_vmem<0>();
         wait_lds();
         block_sync();  // P(tile) and tile+1 are visible; every wave has finished PV(tile-1)
         // Tile+2 goes into the buffer tile-1 used; its addresses were prepared
@@ -523,6 +674,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         // and stalls the issuing waves), the page-table block with the first.
         const char* buf = smem + bo0;
         const char* pb = pbuf0 + (tile & 1) * kPBytes;
+        // Does tile+1 start the next split of the group?
+        next_starts_split = tile + 1 == split_end && tile + 1 < te;
         // PV operands: P^T fragments [u][rb] and V^T fragments of two groups.
         // The first ones are read during the last QK batch so that the first
         // PV MFMA does not wait for them.
@@ -550,7 +703,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         f32x16_t snext;
         const int k1 = (tile + 1) * kKeysPerTile;
         if (tile + 1 < te) {
-          snext = qk_tile(smem + bo1, qreg, k_off, kpe_off, kpe_sw, half, late_part);
+          snext = qk_tile(smem + bo1, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half, late_part);
           // The scores leave the accumulation registers right away (the
           // softmax works on them in VGPRs).
           asm volatile("" : "+v"(snext));
@@ -603,64 +756,30 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         bo1 = bo2;
         bo2 = bt;
       }
+      // Split sp is complete: its partial goes out (a redo pass rewrites
+      // it), and the weight sum of the next split's first tile, taken in the
+      // last iteration, starts the next sum.
+      if (w.S > 1) {
+        emit_partial(c_first + (sp - s_first));
+        l_run = sm.psum;  // every split has at least one tile
+      }
+      } while (++sp < w.s_last);
       wait_vmem<0>();
+    } else {
+      // No key tiles: empty partials (m = -inf, l = 0, O = 0).
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
+      if (w.S > 1)
+        for (int sp = s_first; sp < w.s_last; ++sp) emit_partial(c_first + (sp - s_first));
     }
-    if (!__syncthreads_or(overflow)) break;
+    if (pass == 1 || !__syncthreads_or(overflow)) break;
     m_ref = m_max;
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  // Row statistics travel from the QK owner of each row to every wave.
-  const float l_tot = l_run + swap_halves(l_run);
-  __syncthreads();
-  float2* stats = (float2*)pbuf0;
-  if (half == 0) stats[wave * 32 + qcol] = make_float2(node_ok ? m_ref : NAN, l_tot);
-  __syncthreads();
-  // Accumulator register i of block (f4, rb) holds feature
-  // 32*(4*wave + f4) + (i/4)*8 + 4*half + i%4 of row 32*rb + qcol.
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int r = w.rb * kRows + rb * 32 + qcol;
-    if (r >= a.rows_per_seq) continue;
-    const float2 st = stats[rb * 32 + qcol];
-    const bool ok = !(st.x != st.x);
-    const int64_t g = (int64_t)w.b * a.rows_per_seq + r;
-    if (w.S == 1) {
-      float* dst = a.out + g * kDl;
-      const float mul = ok ? 1.f / st.y : NAN;
-      if (wave == 0 && half == 0 && a.lse) a.lse[g] = ok ? (st.x + __log2f(st.y)) * kLn2 : NAN;
-#pragma unroll
-      for (int f4 = 0; f4 < 4; ++f4)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          f32x4_t v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = oacc[f4 * 4 + rb][4 * gi + e] * mul;
-          *(f32x4_t*)(dst + 32 * (4 * wave + f4) + 8 * gi + 4 * half) = v;
-        }
-    } else {
-      // Split partial: (m, l) in fp32 and the split's own normalised output
-      // O / l in bf16 (half the bytes of the largest store and of the combine's
-      // reads; an empty split stores zeros).
-      const int64_t prow = (int64_t)w.c * a.rows_per_seq + r;
-      __bf16* dst = (__bf16*)a.part_o + prow * kDl;
-      const float mul = (ok && st.y > 0.f) ? 1.f / st.y : 0.f;
-      if (wave == 0 && half == 0) {
-        a.part_ml[2 * prow] = st.x;
-        a.part_ml[2 * prow + 1] = ok ? st.y : NAN;
-      }
-      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-#pragma unroll
-      for (int f4 = 0; f4 < 4; ++f4)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          bf16x4_t v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[f4 * 4 + rb][4 * gi + e] * mul);
-          *(bf16x4_t*)(dst + 32 * (4 * wave + f4) + 8 * gi + 4 * half) = v;
-        }
-    }
-  }
+  // ---- epilogue: a sequence with one split writes its output -------------
+  if (w.S == 1) emit_final();
 }
 
 // ===========================================================================
@@ -796,7 +915,7 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
     mul = node_ok ? 1.f / l_tot : NAN;
     if (half == 0 && a.lse) a.lse[grow] = node_ok ? (m_ref + __log2f(l_tot)) * kLn2 : NAN;
   } else {
-    const int64_t prow = (int64_t)w.c * a.rows_per_seq + r_eff;
+    const int64_t prow = (int64_t)w.c * a.part_rows + r_eff;
     dst = (float*)a.part_o + prow * kDl;
     mul = 1.f;
     if (half == 0) {
@@ -820,8 +939,8 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
 // ===========================================================================
 // Merge the split partials of kCombineRows consecutive query rows of one
 // sequence: M = max m_c, w_c = 2^(m_c - M), L = sum w_c l_c,
-// out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Partials are fp32 O_c (fp32
-// problems) or bf16 O_c / l_c (bf16 problems, weighted by w_c l_c). Each row
+// out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Partials O_c are fp32 (fp32
+// problems) or bf16 (bf16 problems). Each row
 // has 4 groups of 32 lanes (16 features per lane); group g sums the splits
 // c = g (mod 4), and the groups' sums meet in LDS. The rows of a workgroup
 // are adjacent in every split's partial block. Empty splits (m = -inf) get
@@ -834,7 +953,7 @@ constexpr int kCombineStage = 256;
 
 template <typename PartT>
 __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(const VerifyArgs a) {
-  constexpr bool kNormalised = sizeof(PartT) == 2;
+  constexpr bool kBf16 = sizeof(PartT) == 2;
   __shared__ float wsh[kCombineRows][kCombineStage];
   __shared__ float lsh[kCombineRows][kCombineGroups];
   __shared__ f32x4_t accsh[kCombineRows][kCombineGroups - 1][32][4];
@@ -848,8 +967,8 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   if (S <= 1) return;
   const bool live = r < a.rows_per_seq;
   const int rr = live ? r : a.rows_per_seq - 1;
-  const float* ml = a.part_ml + 2 * ((int64_t)s0 * a.rows_per_seq + rr);
-  const int64_t ml_stride = 2 * (int64_t)a.rows_per_seq;
+  const float* ml = a.part_ml + 2 * ((int64_t)s0 * a.part_rows + rr);
+  const int64_t ml_stride = 2 * (int64_t)a.part_rows;
 
   // Row max and NaN flag over the splits (every group computes it).
   float M = -INFINITY;
@@ -866,8 +985,8 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
 
   f32x4_t acc[4] = {};
   float lloc = 0.f;
-  const PartT* po = (const PartT*)a.part_o + ((int64_t)s0 * a.rows_per_seq + rr) * kDl + 16 * t32;
-  const int64_t po_stride = (int64_t)a.rows_per_seq * kDl;
+  const PartT* po = (const PartT*)a.part_o + ((int64_t)s0 * a.part_rows + rr) * kDl + 16 * t32;
+  const int64_t po_stride = (int64_t)a.part_rows * kDl;
   for (int base = 0; base < S; base += kCombineStage) {
     const int cnt = min(kCombineStage, S - base);
     __syncthreads();
@@ -876,7 +995,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
         const float m = ml[(base + cc) * ml_stride];
         const float l = ml[(base + cc) * ml_stride + 1];
         const float wgt = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-        wsh[j][cc] = kNormalised ? wgt * l : wgt;
+        wsh[j][cc] = wgt;
         lloc += wgt * l;
       }
     }
@@ -887,7 +1006,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
     for (int cc = grp; cc < cnt; cc += kCombineGroups) {
       const float wgt = wsh[j][cc];
       const PartT* src = po + (base + cc) * po_stride;
-      if constexpr (kNormalised) {
+      if constexpr (kBf16) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const bf16x8_t v = *(const bf16x8_t*)(src + 8 * q);

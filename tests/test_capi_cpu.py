@@ -64,9 +64,23 @@ def test_forced_and_auto_split_schedules(B):
     info = B.mla_verify_plan_get_info(p)
     assert info["total_splits"] == 256 and info["uses_combine"] == 1
     rows = 32 * 64
-    assert info["grid_blocks"] == 256 * (rows // info["rows_per_block"])
-    # per (split, row): fp32 (m, l) and the bf16 normalised partial output
+    # 256 splits x 16 row blocks: each workgroup runs 16 consecutive splits,
+    # one workgroup per compute unit
+    assert info["splits_per_workgroup"] == 16
+    assert info["grid_blocks"] == 256 // 16 * (rows // info["rows_per_block"])
+    # per (split, row): fp32 (m, l) and the bf16 partial output
     assert ws >= 256 * rows * (2 * 4 + 512 * 2)
+    B.mla_verify_plan_destroy(p)
+    # groups that do not divide the split counts: 3 splits per workgroup,
+    # ceil(40/3) + ceil(32/3) + ceil(40/3) = 14 + 11 + 14 groups, padded to 8 XCDs
+    p, _ = B.mla_verify_plan(3, 64, 16, 1, [3016, 1016, 1516], num_splits=40)
+    info = B.mla_verify_plan_get_info(p)
+    assert info["total_splits"] == 40 + 32 + 40 and info["splits_per_workgroup"] == 3
+    assert info["grid_blocks"] == 40 * 8
+    B.mla_verify_plan_destroy(p)
+    # fp32 problems run one split per workgroup
+    p, _ = B.mla_verify_plan(1, 64, 32, 0, [200032], num_splits=256)
+    assert B.mla_verify_plan_get_info(p)["splits_per_workgroup"] == 1
     B.mla_verify_plan_destroy(p)
     # more splits than key tiles are capped at the tile count
     p, _ = B.mla_verify_plan(2, 4, 4, 1, [40, 100], num_splits=50)

@@ -22,10 +22,11 @@ def _gpu():
     import mla_absorbed_tree_amd.binding  # noqa: F401  (fails loudly if the library is missing)
 
 
-def _full_case(cfg, num_splits=0, **gen_kw):
+def _full_case(cfg, num_splits=0, min_group=1, **gen_kw):
     x = make_inputs(cfg, **gen_kw)
     log("case %s splits=%d" % (cfg, num_splits))
     o, lse, info = run_hip(x, num_splits)
+    assert info["splits_per_workgroup"] >= min_group, info
     o_ref, lse_ref = run_oracle(x)
     compare(o, lse, o_ref, lse_ref, cfg.dtype, "plan=%s" % info)
     return x, o, lse
@@ -85,6 +86,47 @@ def test_bf16_many_heads_rows_span_blocks():
     # 16 nodes x 24 heads = 384 rows = 3 row blocks; nodes straddle block edges.
     cfg = get_config("b1_h64_p4096_t16_bf16", batch=2, heads=24, prefix=517, seed=26)
     _full_case(cfg, 3)
+
+
+# --------------------------------------------------------------------------
+# several consecutive splits per workgroup (one partial written per split)
+# --------------------------------------------------------------------------
+
+def test_split_groups_with_ragged_ends():
+    # 3 sequences of 1000..3000 keys, 40 forced splits (fewer where a sequence
+    # has fewer tiles): 3 splits per workgroup, the last group of a sequence short.
+    cfg = get_config("b1_h64_p4096_t16_bf16", batch=3, prefix_range=(1000, 3000), seed=32)
+    _full_case(cfg, 40, min_group=3)
+
+
+def test_split_groups_partial_row_block_one_tile_splits():
+    # 35 rows (one partial row block); 600 splits of 1-2 tiles, 4 per workgroup.
+    cfg = get_config("b1_h64_p4096_t16_bf16", batch=2, heads=5, tree_nodes=7, prefix=20000, seed=33)
+    _full_case(cfg, 600, min_group=4)
+
+
+def test_split_groups_late_spike_redo():
+    """A prefix key near the end scores ~100 (log2 units) above the rest: the
+    workgroup that meets it late in its group repeats the group with the exact
+    max, rewriting every partial it already wrote."""
+    cfg = get_config("b1_h64_p4096_t16_bf16", batch=2, prefix=4000, seed=34)
+    x = make_inputs(cfg)
+    rng = np.random.default_rng(35)
+    direction = rng.standard_normal(576).astype(np.float32)
+    direction /= np.linalg.norm(direction)
+    x.q_nope[:] = 5.0 * direction[:512]
+    x.q_pe[:] = 5.0 * direction[512:]
+    spike = int(x.kv_indices[int(x.kv_indptr[0]) + 3500])  # slot of prefix position 3500
+    x.kv_c[spike] = 200.0 * direction[:512]
+    x.k_pe[spike] = 200.0 * direction[512:]
+    from gen.inputs import round_to_bf16
+    for a in (x.q_nope, x.q_pe, x.kv_c, x.k_pe):
+        round_to_bf16(a)
+    o, lse, info = run_hip(x, 100)
+    assert info["splits_per_workgroup"] >= 2, info
+    o_ref, lse_ref = run_oracle(x)
+    compare(o, lse, o_ref, lse_ref, "bf16", "plan=%s" % info)
+    assert np.abs(o[:cfg.tree_nodes] - x.kv_c[spike]).max() < 0.05  # sequence 0
 
 
 def test_interleaved_576_wide_cache():

@@ -69,7 +69,15 @@ __device__ __forceinline__ float shfl_f32(float v, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
 }
 // Value held by the lane in the other half of the wave (lane ^ 32).
-__device__ __forceinline__ float swap_halves(float v) { return shfl_f32(v, lane_id() ^ 32); }
+// Value of lane i ^ 32: one v_permlane32_swap (lanes i and i + 32 trade
+// registers; measured layout: lane i < 32 finds lane i + 32's first operand
+// in the second result, lane i + 32 finds lane i's second operand in the
+// first), no LDS round trip.
+__device__ __forceinline__ float swap_halves(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, lane_id() < 32 ? r[1] : r[0]);
+}
 
 // s_waitcnt with only the vector-memory counter bounded (<= N outstanding).
 template <int N>
@@ -336,12 +344,16 @@ __device__ __forceinline__ void issue_tile(const TileLoads& t, int wave) {
   for (int part = 0; part < kTileParts; ++part) issue_tile_part(t, wave, part);
 }
 
-// S^T[32 keys x 32 rows] = K . Q^T for this wave's rows from LDS tile `buf`.
-// Batch 0 is the rope part (both operands from LDS: Q's rope fragments live
-// there, at `qpe` for this lane, to spare 16 registers); batches 1..8 take
-// the latent part of Q from registers. Each batch's LDS reads are issued
-// during the previous batch; the scheduling barriers stop the compiler from
-// hoisting every read at once. between(kb) runs after the MFMAs of batch kb.
+// S^T[32 keys x 32 rows] = K . Q^T for this wave's rows from LDS tile `buf`:
+// 9 batches of 4 MFMAs over the 576 features. Batch kQkRopeBatch is the rope
+// part, with both operands from LDS (Q's rope fragments live there, at `qpe`
+// for this lane, to spare 16 registers); the others take the latent part of Q
+// from registers. First is best (measured: the middle costs 1.5%, the end
+// 18%, where its extra operand registers meet the PV prefetch). Each batch's
+// LDS reads are issued during the previous batch; the scheduling barriers
+// stop the compiler from hoisting every read at once. between(kb) runs after
+// the MFMAs of batch kb.
+constexpr int kQkRopeBatch = 0;
 template <typename Between>
 __device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qreg)[32], const char* qpe, int k_off,
                                             int kpe_off, int kpe_sw, int half, Between&& between) {
@@ -349,29 +361,55 @@ __device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qr
 #pragma unroll
   for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
   bf16x8_t kf[2][4], qf[4];
+  auto load_batch = [&](int b, bf16x8_t (&dst)[4]) {
+    if (b == kQkRopeBatch) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kf[0][j] = *(const bf16x8_t*)(buf + kpe_off + (((2 * j + half) ^ kpe_sw) << 4));
-    qf[j] = *(const bf16x8_t*)(qpe + j * 64 * 16);
-  }
+      for (int j = 0; j < 4; ++j) {
+        dst[j] = *(const bf16x8_t*)(buf + kpe_off + (((2 * j + half) ^ kpe_sw) << 4));
+        qf[j] = *(const bf16x8_t*)(qpe + j * 64 * 16);
+      }
+    } else {
+      const int c0 = 4 * (b < kQkRopeBatch ? b : b - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[j] = *(const bf16x8_t*)(buf + k_off + (c0 + j) * 32);
+    }
+  };
+  load_batch(0, kf[0]);
 #pragma unroll
   for (int kb = 0; kb < 9; ++kb) {
-    if (kb + 1 < 9) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kf[(kb + 1) & 1][j] = *(const bf16x8_t*)(buf + k_off + (4 * kb + j) * 32);
-    }
+    if (kb + 1 < 9) load_batch(kb + 1, kf[(kb + 1) & 1]);
     // Keep the reads of batch kb+1 ahead of the MFMAs of batch kb (left to
     // itself the scheduler sinks them below and reuses the registers).
     __builtin_amdgcn_sched_barrier(0);
+    const int c0 = 4 * (kb < kQkRopeBatch ? kb : kb - 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], kb == 0 ? qf[j] : qreg[4 * (kb - 1) + j], sacc,
-                                                     0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], kb == kQkRopeBatch ? qf[j] : qreg[c0 + j], sacc, 0,
+                                                     0, 0);
     between(kb);
     __builtin_amdgcn_sched_barrier(0);
   }
   return sacc;
 }
+
+// Values 4*gi .. 4*gi+3 of an accumulator block, read out of the
+// accumulation registers one at a time by inline asm: left to itself the
+// compiler moves whole 16-register blocks to VGPRs (which do not fit next to
+// Q) and places the move where it likes. The compiler does not insert the
+// wait states an MFMA result needs before such a read: a caller that may run
+// within 20 cycles of the MFMA that wrote `acc` calls mfma_result_wait()
+// first.
+__device__ __forceinline__ f32x4_t read_acc4(const f32x16_t& acc, int gi) {
+  float t0, t1, t2, t3;
+  asm volatile(
+      "v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\t"
+      "v_accvgpr_read_b32 %2, %6\n\tv_accvgpr_read_b32 %3, %7"
+      : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+      : "a"(acc[4 * gi]), "a"(acc[4 * gi + 1]), "a"(acc[4 * gi + 2]), "a"(acc[4 * gi + 3]));
+  return f32x4_t{t0, t1, t2, t3};
+}
+// 20 wait states: more than any 32x32 MFMA result needs before it is read.
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 15\n\ts_nop 3" ::: "memory"); }
 
 __global__ void __launch_bounds__(bf16k::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_verify_attn_bf16_kernel(const VerifyArgs a) {
@@ -488,29 +526,30 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       sm.mloc = fmaxf(fmaxf(fmaxf(sm.m[0], sm.m[1]), sm.m[2]), fmaxf(fmaxf(sm.m[3], sm.m[4]), sc[15]));
     } else if (k == 3) {
       sm.mswap = swap_halves(sm.mloc);
-    } else if (k == 6) {
+    } else if (k == 4) {
       const float mx = fmaxf(sm.mloc, sm.mswap) * a.scale_log2;  // row max of the tile, log2 units
       m_max = fmaxf(m_max, mx);
       if (m_ref == -INFINITY) m_ref = mx;
       overflow |= mx > m_ref + kOverflowSlack;
       sm.nmu = m_ref == -INFINITY ? 0.f : -m_ref;
       sm.psum = 0.f;
-    } else if (k >= 7 && k < 23) {
-      const int i = k - 7;
+    } else if (k >= 5 && k < 21) {
+      const int i = k - 5;
       sm.p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], a.scale_log2, sm.nmu));
       sm.psum += sm.p[i];
-    } else if (k == 23 || k == 24) {
-      const int u = k - 23;
+    } else if (k == 21 || k == 22) {
+      const int u = k - 21;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) sm.pk[u][jj] = (__bf16)sm.p[8 * u + jj];
-    } else if (k == 25 || k == 26) {
-      const int u = k - 25;
+    } else if (k == 23 || k == 24) {
+      const int u = k - 23;
       *(bf16x8_t*)(pb + ((wave * 2 + u) * 64 + lane) * 16) = sm.pk[u];
-    } else if (k == 27) {
+    } else if (k == 25) {
       if (!next_starts_split) l_run += sm.psum;
     }
   };
-  constexpr int kSoftmaxSteps = 28;
+  constexpr int kSoftmaxSteps = 26;
+  constexpr int kSoftmaxLag = 3;  // PV MFMAs issued before the first softmax step
   auto softmax_to_lds = [&](const f32x16_t& sc, char* pb, bool& overflow) {
 #pragma unroll
     for (int k = 0; k < kSoftmaxSteps; ++k) softmax_step(k, sc, pb, overflow);
@@ -524,18 +563,6 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // in the merge). No exchange between waves, so no barrier.
   // Accumulator register i of block (f4, rb) holds feature
   // 32*(4*wave + f4) + (i/4)*8 + 4*half + i%4 of row 32*rb + qcol.
-  // Values 4*gi .. 4*gi+3 of an accumulator block, read out of the
-  // accumulation registers one at a time (left to itself the compiler moves
-  // whole 16-register blocks to VGPRs, which do not fit next to Q).
-  auto read_acc4 = [](const f32x16_t& acc, int gi) {
-    float t0, t1, t2, t3;
-    asm volatile(
-        "v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\t"
-        "v_accvgpr_read_b32 %2, %6\n\tv_accvgpr_read_b32 %3, %7"
-        : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
-        : "a"(acc[4 * gi]), "a"(acc[4 * gi + 1]), "a"(acc[4 * gi + 2]), "a"(acc[4 * gi + 3]));
-    return f32x4_t{t0, t1, t2, t3};
-  };
   //
   // The partial arrays have a.part_rows (a multiple of kRows) rows per split,
   // so the rows past rows_per_seq of the last row block have room and every
@@ -549,6 +576,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     const int qcol = lq & 31, half = lq >> 5;
     const float l_tot = l_run + swap_halves(l_run);
     const bool node_ok = row_anc() != 0;
+    mfma_result_wait();  // the last PV MFMAs may have just been issued
     // (m, l) of the row; both lanes of a row hold the same values.
     const int64_t prow = (int64_t)c * a.part_rows + w.rb * kRows + wave * 32 + qcol;
     *(float2*)(a.part_ml + 2 * prow) = make_float2(node_ok ? m_ref : NAN, node_ok ? l_tot : NAN);
@@ -588,6 +616,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     const float l_tot = l_run + swap_halves(l_run);
     float2* stats = (float2*)pbuf0;  // the P buffers are free after the loop
     const bool node_ok = row_anc() != 0;
+    mfma_result_wait();
     __syncthreads();
     if (half == 0) stats[wave * 32 + qcol] = make_float2(node_ok ? m_ref : NAN, l_tot);
     __syncthreads();
@@ -698,23 +727,21 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
             load_v(0, vf[0]);
           }
         };
-        // Scores of tile+1. On the last tile there is none: all -inf makes the
-        // softmax step below a no-op for the row state.
+        // Scores of tile+1. On the last tile there is none: all -inf (set in
+        // the PV loop) makes the softmax steps a no-op for the row state.
         f32x16_t snext;
         const int k1 = (tile + 1) * kKeysPerTile;
-        if (tile + 1 < te) {
+        const bool has_next = tile + 1 < te;
+        if (has_next) {
           snext = qk_tile(smem + bo1, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half, late_part);
-          // The scores leave the accumulation registers right away (the
-          // softmax works on them in VGPRs).
-          asm volatile("" : "+v"(snext));
-          if (needs_mask(k1)) mask_tile(snext, k1);
         } else {
           issue_tile(pending, wave);
           issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
           load_p(0);
           load_v(0, vf[0]);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) snext[i] = -INFINITY;
+          // snext stays unset here: it is set to -inf below (a value
+          // assigned here would make the compiler move the QK result out of
+          // the accumulation registers right after the QK, to merge the two).
         }
         __builtin_amdgcn_sched_barrier(0);
 
@@ -740,12 +767,28 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
             const bf16x8_t va = __builtin_bit_cast(
                 bf16x8_t, __builtin_shufflevector(vf[g & 1][0], vf[g & 1][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
+            for (int rr = 0; rr < 4; ++rr) {
+              const int rb = (rr + 1) & 3;  // row block 0 last (see below)
               const int f4 = g & 3;
               oacc[f4 * 4 + rb] =
                   __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbr[g >> 2][rb], oacc[f4 * 4 + rb], 0, 0, 0);
-              const int k = 4 * g + rb;
-              if (k < kSoftmaxSteps) softmax_step(k, snext, pbuf0 + ((tile + 1) & 1) * kPBytes, overflow);
+              const int k = 4 * g + rr;
+              if (k == kSoftmaxLag - 1) {
+                // The scores of tile+1 leave the accumulation registers only
+                // here, behind the first PV MFMAs: read right after the last
+                // QK MFMA they would stall the wave until the matrix pipe
+                // drains. (The compiler parks the QK accumulator where an
+                // output block lives; that block's first MFMA comes after.)
+                asm volatile("" : "+v"(snext));
+                if (!has_next) {
+#pragma unroll
+                  for (int i = 0; i < 16; ++i) snext[i] = -INFINITY;
+                } else if (needs_mask(k1)) {
+                  mask_tile(snext, k1);
+                }
+              }
+              if (k >= kSoftmaxLag && k - kSoftmaxLag < kSoftmaxSteps)
+                softmax_step(k - kSoftmaxLag, snext, pbuf0 + ((tile + 1) & 1) * kPBytes, overflow);
               prepare_step(k);
               __builtin_amdgcn_sched_barrier(0);
             }

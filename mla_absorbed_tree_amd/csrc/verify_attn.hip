@@ -4,16 +4,20 @@
 // over the prefix and the node's ancestor-or-self tree tail, softmax, then the
 // weighted sum of kv_c (latent-space output) and the log-sum-exp.
 //
-// Work decomposition: one workgroup per (sequence b, block of query rows, KV
-// split). Every key tile (kv_c | k_pe) is staged in LDS once and serves all
-// query rows of the block, so the head-shared latent is read from L2 once per
-// block instead of once per head.
+// Work decomposition: one workgroup per (sequence b, block of query rows,
+// group of consecutive KV splits). Every key tile (kv_c | k_pe) is staged in
+// LDS once and serves all query rows of the block, so the head-shared latent
+// is read from L2 once per block instead of once per head. A workgroup with
+// several splits streams their tiles through one pipeline and writes one
+// partial per split.
 //
 // bf16 kernel: 4 waves, 128 query rows, 32-key tiles.
-//   * A 4-deep LDS ring of key tiles is filled by global_load_lds_dwordx4
-//     (global -> LDS without registers), 3 tiles ahead of the tile in use.
-//   * QK: wave w owns query rows 32w..32w+31 and keeps their Q (576 bf16) in
-//     VGPRs. S^T[32 keys x 32 rows] = K . Q^T with 36 mfma_f32_32x32x16_bf16.
+//   * A 3-deep LDS ring of key tiles is filled by global_load_lds_dwordx4
+//     (global -> LDS without registers); the loads of tile t+2 go out while
+//     tiles t and t+1 are computed on.
+//   * QK: wave w owns query rows 32w..32w+31 and keeps the latent 512
+//     features of their Q in VGPRs (the rope 64 in LDS). S^T[32 keys x 32
+//     rows] = K . Q^T with 36 mfma_f32_32x32x16_bf16.
 //   * Softmax weights in fp32 (exp2 domain) against a per-row reference max,
 //     rounded to bf16 and shared through LDS (P, 8 KB per tile).
 //   * PV: wave w owns output features 128w..128w+127 of all 128 rows:

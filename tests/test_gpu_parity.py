@@ -105,6 +105,21 @@ def test_split_groups_partial_row_block_one_tile_splits():
     _full_case(cfg, 600, min_group=4)
 
 
+def test_split_groups_paged_nan_poison():
+    # page_size=1 pool with NaN in every unused slot; 16 forced splits per
+    # sequence, 2 per workgroup.
+    cfg = get_config("b8_h64_paged600k_t16_bf16", batch=5, prefix_range=(600, 2000), pool_slots=20000,
+                     seed=36)
+    _full_case(cfg, 16, min_group=2, poison_unused=True)
+
+
+def test_split_groups_tree64_tail_spans_tiles():
+    # 64-node tree (its tail spans two key tiles), 32 row blocks, 16 splits,
+    # 2 per workgroup: the last split of each group holds the masked tail.
+    cfg = get_config("b4_h64_p32768_t64_bf16", batch=1, prefix=2000, seed=37)
+    _full_case(cfg, 16, min_group=2)
+
+
 def test_split_groups_late_spike_redo():
     """A prefix key near the end scores ~100 (log2 units) above the rest: the
     workgroup that meets it late in its group repeats the group with the exact

@@ -1032,7 +1032,11 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
 
   f32x4_t acc[4] = {};
   float lloc = 0.f;
-  const PartT* po = (const PartT*)a.part_o + ((int64_t)s0 * a.part_rows + rr) * kDl + 16 * t32;
+  // Lane t32 of a group holds 16 of the row's 512 features: for bf16 the
+  // 8-feature runs starting at 8*t32 and 256 + 8*t32, for fp32 the 4-feature
+  // runs at 4*t32 + 128*q, so that each load instruction of a group reads
+  // 512 contiguous bytes.
+  const PartT* po = (const PartT*)a.part_o + ((int64_t)s0 * a.part_rows + rr) * kDl + (kBf16 ? 8 : 4) * t32;
   const int64_t po_stride = (int64_t)a.part_rows * kDl;
   for (int base = 0; base < S; base += kCombineStage) {
     const int cnt = min(kCombineStage, S - base);
@@ -1056,7 +1060,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
       if constexpr (kBf16) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const bf16x8_t v = *(const bf16x8_t*)(src + 8 * q);
+          const bf16x8_t v = *(const bf16x8_t*)(src + 256 * q);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             acc[2 * q][e] += wgt * (float)v[e];
@@ -1065,7 +1069,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += wgt * *(const f32x4_t*)(src + 4 * q);
+        for (int q = 0; q < 4; ++q) acc[q] += wgt * *(const f32x4_t*)(src + 128 * q);
       }
     }
   }
@@ -1084,7 +1088,11 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   const int64_t grow = (int64_t)b * a.rows_per_seq + r;
   const float inv = nan ? NAN : 1.f / lloc;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) *(f32x4_t*)(a.out + grow * kDl + 16 * t32 + 4 * q) = acc[q] * inv;
+  for (int q = 0; q < 4; ++q) {
+    // acc[q]: features 8*t32 + 256*(q/2) + 4*(q%2) (bf16) or 4*t32 + 128*q (fp32).
+    const int f = kBf16 ? 8 * t32 + 256 * (q >> 1) + 4 * (q & 1) : 4 * t32 + 128 * q;
+    *(f32x4_t*)(a.out + grow * kDl + f) = acc[q] * inv;
+  }
   if (t32 == 0 && a.lse) a.lse[grow] = nan ? NAN : (M + __log2f(lloc)) * kLn2;
 }
 

@@ -137,21 +137,28 @@ def bench_workload(name, steps, warmup, num_splits=None):
     return res, x
 
 
+def kernel_source_digest():
+    """sha256 of the kernel source with its // comments and blank lines removed:
+    it changes with the code, not with its comments."""
+    import hashlib
+    src = os.path.join(ROOT, "mla_absorbed_tree_amd", "csrc", "verify_attn.hip")
+    with open(src) as f:
+        lines = [ln.split("//", 1)[0].rstrip() for ln in f]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per attention launch from the committed rocprofv3 counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None when
-    the kernel source changed since they were taken."""
-    import hashlib
-    src = os.path.join(ROOT, "mla_absorbed_tree_amd", "csrc", "verify_attn.hip")
+    the kernel code changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             prof = json.load(f)
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_digest()
     except OSError:
         return None
-    if prof.get("kernel_source_sha256") != sha:
+    if prof.get("kernel_code_sha256") != sha:
         return None
     w = prof.get("workloads", {}).get(workload)
     return None if w is None else float(w["traffic_bytes"])

@@ -239,7 +239,11 @@ constexpr int kAncBytes = kRows * 8;                          // ancestor mask o
 constexpr int kQpeBytes = kRows * kDr * 2;                     // 16384
 constexpr int kSmem = kNbuf * kBufBytes + 2 * kPBytes + kIdxBytes + kAncBytes + kQpeBytes;
 // Vector-memory stores one wave issues for a split partial: (m, l) plus
-// 4 row blocks x 4 feature blocks x 2 16-byte pieces.
+// 4 row blocks x 4 feature blocks x 2 16-byte pieces. The wait after a split
+// boundary lets this many operations stay outstanding; it is safe as long as
+// the compiler emits at least this many store instructions, which holds
+// because no two of these stores are adjacent in memory (none can merge) and
+// none is wider than the widest store instruction.
 constexpr int kPartialStores = 1 + 4 * 4 * 2;
 // Vector-memory instructions each wave issues per tile: 8 kv_c rows, one
 // block of 8 k_pe rows, one block of 8 page-table entries.

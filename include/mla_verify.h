@@ -60,7 +60,8 @@ typedef struct {
   int32_t d_rope;           /* must be 64 */
   int32_t dtype;            /* mla_dtype of q_nope, q_pe, kv_c and k_pe; out/lse are fp32 */
   const int32_t* kv_len_host; /* host [batch]: N_b = P_b + T tokens of sequence b (>= T).
-                                 Read during the call only; sizes the split schedule. */
+                                 Read during the call only; sizes the split schedule
+                                 (the lengths a run sees may differ, see mla_verify_run). */
   int32_t num_splits;       /* 0 = planner's choice; > 0 forces that many KV splits
                                for every sequence (capped at its number of key tiles) */
   int64_t kv_c_row_stride;  /* elements between consecutive kv_c slots (>= 512, multiple of 8) */
@@ -102,7 +103,11 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
  *   k_pe        device, slot s at k_pe + s*k_pe_row_stride, 64 elements
  *               (kv_c and k_pe may interleave inside one 576-wide buffer)
  *   kv_indptr   device int32 [batch+1]; kv_indptr[0] = 0 and
- *               kv_indptr[b+1] - kv_indptr[b] = kv_len_host[b] of the plan
+ *               N_b = kv_indptr[b+1] - kv_indptr[b] >= T.  N_b may differ from
+ *               the plan's kv_len_host[b] (one plan, or one captured graph,
+ *               serves decode steps whose lengths change on the device): each
+ *               sequence keeps the plan's split count over its actual length,
+ *               and a split left without keys contributes nothing.
  *   kv_indices  device int32 [kv_indptr[batch]]: slot of logical position j of
  *               sequence b at kv_indices[kv_indptr[b] + j] (page_size = 1).
  *               Positions 0..P_b-1 are the prefix, P_b..P_b+T-1 the tree nodes.

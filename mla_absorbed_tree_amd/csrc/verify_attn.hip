@@ -576,13 +576,13 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // so the rows past rows_per_seq of the last row block have room and every
   // store below is unconditional: exactly kPartialStores vector-memory
   // instructions, which the wait after a split boundary relies on.
-  auto emit_partial = [&](int c) {
+  auto emit_partial = [&](int c, float l_part) {
     // Lane indices taken afresh (an opaque copy), so that no address below is
     // computed ahead of the tile loop and kept live through it.
     int lq = lane;
     asm volatile("" : "+v"(lq));
     const int qcol = lq & 31, half = lq >> 5;
-    const float l_tot = l_run + swap_halves(l_run);
+    const float l_tot = l_part + swap_halves(l_part);
     const bool node_ok = row_anc() != 0;
     mfma_result_wait();  // the last PV MFMAs may have just been issued
     // (m, l) of the row; both lanes of a row hold the same values.
@@ -809,10 +809,16 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       }
       // Split sp is complete: its partial goes out (a redo pass rewrites
       // it), and the weight sum of the next split's first tile, taken in the
-      // last iteration, starts the next sum.
+      // last iteration, starts the next sum. A split can be empty when the
+      // sequence is shorter than the plan assumed: its partial has l = 0 and
+      // O = 0, and the carried sum waits for the next split with tiles.
       if (w.S > 1) {
-        emit_partial(c_first + (sp - s_first));
-        l_run = sm.psum;  // every split has at least one tile
+        if (split_end > split_begin) {
+          emit_partial(c_first + (sp - s_first), l_run);
+          l_run = sm.psum;
+        } else {
+          emit_partial(c_first + (sp - s_first), 0.f);
+        }
       }
       } while (++sp < w.s_last);
       wait_vmem<0>();
@@ -823,7 +829,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
       if (w.S > 1)
-        for (int sp = s_first; sp < w.s_last; ++sp) emit_partial(c_first + (sp - s_first));
+        for (int sp = s_first; sp < w.s_last; ++sp) emit_partial(c_first + (sp - s_first), 0.f);
     }
     if (pass == 1 || !__syncthreads_or(overflow)) break;
     m_ref = m_max;

@@ -14,8 +14,9 @@ _DTYPES = {"bf16": (B.MLA_DTYPE_BF16, torch.bfloat16), "f32": (B.MLA_DTYPE_F32, 
 class MlaVerify:
     """One planned tree-verify problem: call it with device tensors.
 
-    kv_lens are the host copies of N_b (prefix + tree nodes per sequence); the
-    device kv_indptr passed at call time must describe the same lengths.
+    kv_lens are the host copies of N_b (prefix + tree nodes per sequence) that
+    size the split schedule; the device kv_indptr passed at call time may
+    describe other lengths (each still >= tree_nodes).
     """
 
     def __init__(self, batch: int, heads: int, tree_nodes: int, dtype: str,

@@ -78,3 +78,59 @@ def test_graph_replays_match_eager(name, over):
     assert torch.equal(out, new_o) and torch.equal(lse, new_l)
     del g
     mv.close()
+
+
+def test_one_plan_and_graph_across_decode_steps():
+    """One plan and one captured graph serve two decode steps whose lengths,
+    slot tables, trees and queries change in place on the device. The second
+    step's middle sequence is far shorter than planned, so 45 of its 48 splits
+    get no keys; each workgroup runs 4 splits, so empty splits also sit inside
+    groups that have keys."""
+    import dataclasses
+    from gpu_util import compare, run_oracle
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+    cfg = get_config("b8_h64_paged600k_t16_bf16", batch=3, pool_slots=8000, seed=40)
+    steps = [make_inputs(cfg, prefix_lens=np.array([1800, 1600, 2000])),
+             make_inputs(dataclasses.replace(cfg, seed=41), prefix_lens=np.array([1900, 60, 2100]))]
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, steps[0].kv_lens, 48)
+    assert mv.info["splits_per_workgroup"] == 4, mv.info
+    d = device_inputs(steps[0])
+    cap = max(len(x.kv_indices) for x in steps)
+    idx = torch.zeros(cap, dtype=torch.int32, device="cuda")
+    idx[:len(steps[0].kv_indices)] = d["kv_indices"]
+    args = [d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"], idx, d["tree_parents"]]
+    rows = cfg.batch * cfg.tree_nodes
+    out = torch.empty((rows, cfg.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows, cfg.heads), dtype=torch.float32, device="cuda")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mv(*args, steps[0].scale, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mv(*args, steps[0].scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+
+    for k, x in enumerate(steps):
+        if k > 0:  # the next step's data, written in place
+            nd = device_inputs(x)
+            for name, t in zip(("q_nope", "q_pe", "kv_c", "k_pe", "kv_indptr"), args[:5]):
+                t.copy_(nd[name])
+            idx.zero_()
+            idx[:len(x.kv_indices)] = nd["kv_indices"]
+            args[6].copy_(nd["tree_parents"])
+            torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        o_ref, lse_ref = run_oracle(x)
+        compare(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, cfg.dtype, "step %d" % k)
+        eo, el = mv(*args, x.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(eo, out) and torch.equal(el, lse), "step %d: replay differs from eager" % k
+    del g
+    mv.close()

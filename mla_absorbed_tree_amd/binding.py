@@ -25,11 +25,11 @@ MLA_DTYPE_BF16 = 1
 MLA_VERIFY_MAX_BATCH = 256
 MLA_VERIFY_MAX_TREE = 64
 
-# Symbols declared in include/mla_verify.h.
+# Symbols declared in include/mla_verify.h and include/mla_kv_compact.h.
 EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
                     "mla_verify_attend", "mla_verify_combine",
                     "mla_verify_tree_masks", "mla_verify_plan_destroy",
-                    "mla_verify_status_string", "mla_verify_last_error")
+                    "mla_verify_status_string", "mla_verify_last_error", "mla_kv_compact")
 
 
 class MlaVerifyError(RuntimeError):
@@ -69,15 +69,15 @@ def _load():
     lib.mla_verify_combine.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.mla_verify_tree_masks.argtypes = [vp, i32, i32, vp, vp]
     lib.mla_verify_plan_destroy.argtypes = [vp]
+    lib.mla_kv_compact.argtypes = [i32, i32, i64, vp, vp, i64, i64, vp, vp, vp, vp, i64, i64, i32, vp, vp]
     lib.mla_verify_status_string.argtypes = [i32]
     lib.mla_verify_status_string.restype = ctypes.c_char_p
     lib.mla_verify_last_error.argtypes = []
     lib.mla_verify_last_error.restype = ctypes.c_char_p
     for name in ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
                  "mla_verify_attend", "mla_verify_combine", "mla_verify_tree_masks",
-                 "mla_verify_plan_destroy"):
+                 "mla_verify_plan_destroy", "mla_kv_compact"):
         getattr(lib, name).restype = i32
-    del i64
     return lib
 
 
@@ -183,3 +183,14 @@ def mla_verify_combine(plan, out, lse, workspace, workspace_bytes: Optional[int]
 def mla_verify_tree_masks(tree_parents, batch: int, tree_nodes: int, masks, stream=None) -> None:
     _check(_lib.mla_verify_tree_masks(_ptr(tree_parents), int(batch), int(tree_nodes), _ptr(masks),
                                       _stream_handle(stream)))
+
+
+def mla_kv_compact(dtype: int, batch: int, total_tokens: int, kv_c, k_pe, kv_c_row_stride: int,
+                   k_pe_row_stride: int, kv_indptr, kv_indices, dst_kv_c, dst_k_pe,
+                   dst_kv_c_row_stride: int, dst_k_pe_row_stride: int, dst_base: int,
+                   new_kv_indices, stream=None) -> None:
+    _check(_lib.mla_kv_compact(int(dtype), int(batch), int(total_tokens), _ptr(kv_c), _ptr(k_pe),
+                               int(kv_c_row_stride), int(k_pe_row_stride), _ptr(kv_indptr),
+                               _ptr(kv_indices), _ptr(dst_kv_c), _ptr(dst_k_pe),
+                               int(dst_kv_c_row_stride), int(dst_k_pe_row_stride), int(dst_base),
+                               _ptr(new_kv_indices), _stream_handle(stream)))

@@ -1,12 +1,15 @@
 // extern "C" entry points of libmlaverify: argument checks, plan objects and
 // the launch sequence. Device work happens only inside the launchers.
+#include <climits>
 #include <cstdint>
 #include <cstring>
 #include <new>
 #include <string>
 
+#include "../../include/mla_kv_compact.h"
 #include "../../include/mla_verify.h"
 #include "kernel_params.h"
+#include "kv_compact_params.h"
 #include "plan.h"
 
 struct mla_verify_plan_s {
@@ -177,6 +180,50 @@ mla_status mla_verify_tree_masks(const int32_t* tree_parents, int32_t batch, int
     return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 and tree_nodes in 1..64");
   const int e = mlav::launch_tree_masks(tree_parents, batch, tree_nodes, masks, stream);
   if (e != 0) return fail(MLA_ERR_HIP, "tree mask launch failed (hipError " + std::to_string(e) + ")");
+  return MLA_OK;
+}
+
+mla_status mla_kv_compact(int32_t dtype, int32_t batch, int64_t total_tokens, const void* kv_c,
+                          const void* k_pe, int64_t kv_c_row_stride, int64_t k_pe_row_stride,
+                          const int32_t* kv_indptr, const int32_t* kv_indices, void* dst_kv_c,
+                          void* dst_k_pe, int64_t dst_kv_c_row_stride, int64_t dst_k_pe_row_stride,
+                          int32_t dst_base, int32_t* new_kv_indices, void* stream) {
+  g_last_error.clear();
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32)
+    return fail(MLA_ERR_INVALID_ARG, "dtype must be MLA_DTYPE_F32 or MLA_DTYPE_BF16");
+  if (batch < 1 || batch > MLA_VERIFY_MAX_BATCH)
+    return fail(MLA_ERR_INVALID_ARG, "batch must be in 1.." + std::to_string(MLA_VERIFY_MAX_BATCH));
+  if (total_tokens < 0) return fail(MLA_ERR_INVALID_ARG, "total_tokens < 0");
+  if (dst_base < 0 || int64_t(dst_base) + total_tokens > int64_t(INT32_MAX))
+    return fail(MLA_ERR_INVALID_ARG, "dst_base + total_tokens must fit in int32 (dst_base >= 0)");
+  if (kv_c_row_stride < 512 || k_pe_row_stride < 64 || dst_kv_c_row_stride < 512 ||
+      dst_k_pe_row_stride < 64 || kv_c_row_stride % 8 || k_pe_row_stride % 8 ||
+      dst_kv_c_row_stride % 8 || dst_k_pe_row_stride % 8)
+    return fail(MLA_ERR_INVALID_ARG, "row strides must be >= 512 (kv_c) / 64 (k_pe) and multiples of 8");
+  if (!kv_c || !k_pe || !kv_indptr || !kv_indices || !dst_kv_c || !dst_k_pe || !new_kv_indices)
+    return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(kv_c) || !aligned16(k_pe) || !aligned16(dst_kv_c) || !aligned16(dst_k_pe))
+    return fail(MLA_ERR_INVALID_ARG, "kv_c, k_pe and the destination pool must be 16-byte aligned");
+  if (new_kv_indices == kv_indices) return fail(MLA_ERR_INVALID_ARG, "new_kv_indices may not alias kv_indices");
+  if (total_tokens == 0) return MLA_OK;
+  const int64_t es = dtype == MLA_DTYPE_BF16 ? 2 : 4;
+  mlav::KvCompactArgs a{};
+  a.kv_c = kv_c;
+  a.k_pe = k_pe;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.dst_kv_c = dst_kv_c;
+  a.dst_k_pe = dst_k_pe;
+  a.new_indices = new_kv_indices;
+  a.kv_c_stride_bytes = kv_c_row_stride * es;
+  a.k_pe_stride_bytes = k_pe_row_stride * es;
+  a.dst_kv_c_stride_bytes = dst_kv_c_row_stride * es;
+  a.dst_k_pe_stride_bytes = dst_k_pe_row_stride * es;
+  a.total = total_tokens;
+  a.batch = batch;
+  a.dst_base = dst_base;
+  const int e = mlav::launch_kv_compact(a, int(es), stream);
+  if (e != 0) return fail(MLA_ERR_HIP, "kv compaction launch failed (hipError " + std::to_string(e) + ")");
   return MLA_OK;
 }
 

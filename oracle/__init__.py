@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the library or its binding.
 """
+from .kv_compact_oracle import kv_compact
 from .mla_verify_oracle import (brute_force_verify, chunk_partial, merge_partials, node_scores,
                                 tree_ancestors, verify_attention, visible_positions)
 
-__all__ = ["brute_force_verify", "chunk_partial", "merge_partials", "node_scores",
+__all__ = ["brute_force_verify", "chunk_partial", "kv_compact", "merge_partials", "node_scores",
            "tree_ancestors", "verify_attention", "visible_positions"]

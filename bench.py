@@ -5,7 +5,9 @@ One step = one pass of the whole path (tree masks + split-KV attention + LSE
 combine, i.e. mla_verify_attend followed by mla_verify_combine) over one batch
 of synthetic inputs that already sit in HBM. The primary workload is the
 32k-prefix batch (B=4, H=64, P=32768, T=64, bf16); the 200k-prefix workload
-(B=1, H=64, P=200000, T=32, 256 splits) is reported in "also".
+(B=1, H=64, P=200000, T=32, 256 splits) is reported in "also", and the KV
+compaction of the paged workload's 600k-slot pool (its kernel's HBM rate, and
+the verify step on the scattered against the compacted pool) in "kv_compact".
 
 Prints ONE JSON line. `value` is KV tokens/s (sum of N_b per step / step time);
 `roofline` describes the attention kernel (algorithmic FLOPs per launch over
@@ -137,6 +139,63 @@ def bench_workload(name, steps, warmup, num_splits=None):
     return res, x
 
 
+def bench_kv_compact(steps, warmup, name="b8_h64_paged600k_t16_bf16"):
+    """KV-cache compaction of the paged workload's pool (page_size=1, 600k
+    slots): the compaction kernel's time and HBM rate, and the verify step on
+    the scattered pool against the same step on the compacted pool."""
+    import torch
+    from gen import get_config, make_inputs
+    from mla_absorbed_tree_amd import binding as B
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+
+    cfg = get_config(name)
+    log("[bench] kv compaction on %s" % name)
+    x = make_inputs(cfg)
+    d = device_inputs(x)
+    n = int(x.kv_indptr[-1])
+    dc = torch.empty((n, 512), dtype=torch.bfloat16, device="cuda")
+    dp = torch.empty((n, 64), dtype=torch.bfloat16, device="cuda")
+    new = torch.empty(n, dtype=torch.int32, device="cuda")
+
+    def compact():
+        B.mla_kv_compact(B.MLA_DTYPE_BF16, cfg.batch, n, d["kv_c"], d["k_pe"], 512, 64, d["kv_indptr"],
+                         d["kv_indices"], dc, dp, 512, 64, 0, new)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    t_compact = timed(compact)
+    # bytes the compaction must move: every row read and written once, plus
+    # the page table read and the new one written
+    nbytes = 2 * n * (512 + 64) * 2 + 2 * n * 4
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, 0)
+    rows = cfg.batch * cfg.tree_nodes
+    out = torch.empty((rows, cfg.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows, cfg.heads), dtype=torch.float32, device="cuda")
+    common = (d["q_nope"], d["q_pe"])
+    t_scattered = timed(lambda: mv(*common, d["kv_c"], d["k_pe"], d["kv_indptr"], d["kv_indices"],
+                                   d["tree_parents"], x.scale, out=out, lse=lse))
+    t_compacted = timed(lambda: mv(*common, dc, dp, d["kv_indptr"], new, d["tree_parents"], x.scale,
+                                   out=out, lse=lse))
+    mv.close()
+    gbps = nbytes / (t_compact * 1e-3) / 1e9
+    del d, dc, dp, new
+    torch.cuda.empty_cache()
+    return {"workload": name, "tokens": n, "ms": t_compact, "bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                         "frac": gbps * 1e9 / PEAK_HBM_BYTES, "kernel": "mla_kv_compact_kernel"},
+            "verify_step_ms_scattered": t_scattered, "verify_step_ms_compacted": t_compacted}
+
+
 def kernel_source_digest():
     """sha256 of the kernel source with its // comments and blank lines removed:
     it changes with the code, not with its comments."""
@@ -201,6 +260,7 @@ def main():
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-also", action="store_true", help="skip the 200k-prefix workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compact", action="store_true", help="skip the KV-compaction measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (reference for HBM counters)")
@@ -226,6 +286,9 @@ def main():
         r2, _ = bench_workload(ALSO, a.steps, a.warmup)
         also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "hbm_gbps", "hbm_frac",
                                         "mfma_frac", "kernels_ms", "roofline", "config", "plan")})
+    compact = None
+    if not a.no_also and not a.no_compact:
+        compact = bench_kv_compact(a.steps, a.warmup)
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the float64 oracle on a bounded sample")
@@ -253,6 +316,7 @@ def main():
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "also": also,
+        "kv_compact": compact,
     }
     print(json.dumps(line), flush=True)
 

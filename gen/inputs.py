@@ -163,3 +163,26 @@ def make_inputs(cfg: VerifyConfig, *, poison_unused: bool = False,
                         kv_indptr=indptr.astype(np.int32), kv_indices=indices,
                         parents=parents.astype(np.int32), prefix_lens=P,
                         scale=float(cfg.scale))
+
+
+def make_accept_tokens(rng: np.random.Generator, parents: np.ndarray, vocab: int = 4,
+                       p_match: float = 0.8):
+    """Synthetic draft and target tokens for one draft tree, for token acceptance.
+
+    The target's token after each node and after the prefix are uniform over
+    ``vocab``; a node's draft token copies the target's token after its parent
+    (after the prefix for a root) with probability ``p_match``, else it is
+    uniform. Returns (draft [T], target [T], root_target) as int32 / int.
+    Invalid parents (the generator does not draw them; tests plant them) are
+    treated as roots here.
+    """
+    T = len(parents)
+    target = rng.integers(0, vocab, size=T).astype(np.int32)
+    root_target = int(rng.integers(0, vocab))
+    draft = rng.integers(0, vocab, size=T).astype(np.int32)
+    copy = rng.random(T) < p_match
+    for t in range(T):
+        if copy[t]:
+            p = int(parents[t])
+            draft[t] = target[p] if 0 <= p < t else root_target
+    return draft, target, root_target

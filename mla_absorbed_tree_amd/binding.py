@@ -25,11 +25,12 @@ MLA_DTYPE_BF16 = 1
 MLA_VERIFY_MAX_BATCH = 256
 MLA_VERIFY_MAX_TREE = 64
 
-# Symbols declared in include/mla_verify.h and include/mla_kv_compact.h.
+# Symbols declared in include/*.h.
 EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
                     "mla_verify_attend", "mla_verify_combine",
                     "mla_verify_tree_masks", "mla_verify_plan_destroy",
-                    "mla_verify_status_string", "mla_verify_last_error", "mla_kv_compact")
+                    "mla_verify_status_string", "mla_verify_last_error", "mla_kv_compact",
+                    "mla_tree_accept")
 
 
 class MlaVerifyError(RuntimeError):
@@ -70,13 +71,14 @@ def _load():
     lib.mla_verify_tree_masks.argtypes = [vp, i32, i32, vp, vp]
     lib.mla_verify_plan_destroy.argtypes = [vp]
     lib.mla_kv_compact.argtypes = [i32, i32, i64, vp, vp, i64, i64, vp, vp, vp, vp, i64, i64, i32, vp, vp]
+    lib.mla_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
     lib.mla_verify_status_string.argtypes = [i32]
     lib.mla_verify_status_string.restype = ctypes.c_char_p
     lib.mla_verify_last_error.argtypes = []
     lib.mla_verify_last_error.restype = ctypes.c_char_p
     for name in ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
                  "mla_verify_attend", "mla_verify_combine", "mla_verify_tree_masks",
-                 "mla_verify_plan_destroy", "mla_kv_compact"):
+                 "mla_verify_plan_destroy", "mla_kv_compact", "mla_tree_accept"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -194,3 +196,10 @@ def mla_kv_compact(dtype: int, batch: int, total_tokens: int, kv_c, k_pe, kv_c_r
                                _ptr(kv_indices), _ptr(dst_kv_c), _ptr(dst_k_pe),
                                int(dst_kv_c_row_stride), int(dst_k_pe_row_stride), int(dst_base),
                                _ptr(new_kv_indices), _stream_handle(stream)))
+
+
+def mla_tree_accept(tree_parents, draft_tokens, target_tokens, root_targets, batch: int,
+                    tree_nodes: int, accept_len, accept_path, bonus_token, stream=None) -> None:
+    _check(_lib.mla_tree_accept(_ptr(tree_parents), _ptr(draft_tokens), _ptr(target_tokens),
+                                _ptr(root_targets), int(batch), int(tree_nodes), _ptr(accept_len),
+                                _ptr(accept_path), _ptr(bonus_token), _stream_handle(stream)))

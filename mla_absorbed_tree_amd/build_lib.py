@@ -15,7 +15,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmlaverify.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["verify_attn.hip", "kv_compact.hip"]
+HIP_SOURCES = ["verify_attn.hip", "kv_compact.hip", "tree_accept.hip"]
 CXX_SOURCES = ["plan.cpp", "capi.cpp"]
 
 # Packed fp32 VALU forms are kept out of the generated code on purpose.

@@ -7,6 +7,7 @@
 #include <string>
 
 #include "../../include/mla_kv_compact.h"
+#include "../../include/mla_tree_accept.h"
 #include "../../include/mla_verify.h"
 #include "kernel_params.h"
 #include "kv_compact_params.h"
@@ -224,6 +225,22 @@ mla_status mla_kv_compact(int32_t dtype, int32_t batch, int64_t total_tokens, co
   a.dst_base = dst_base;
   const int e = mlav::launch_kv_compact(a, int(es), stream);
   if (e != 0) return fail(MLA_ERR_HIP, "kv compaction launch failed (hipError " + std::to_string(e) + ")");
+  return MLA_OK;
+}
+
+mla_status mla_tree_accept(const int32_t* tree_parents, const int32_t* draft_tokens,
+                           const int32_t* target_tokens, const int32_t* root_targets, int32_t batch,
+                           int32_t tree_nodes, int32_t* accept_len, int32_t* accept_path,
+                           int32_t* bonus_token, void* stream) {
+  g_last_error.clear();
+  if (!tree_parents || !draft_tokens || !target_tokens || !root_targets || !accept_len || !accept_path ||
+      !bonus_token)
+    return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
+  if (batch < 1 || tree_nodes < 1 || tree_nodes > MLA_VERIFY_MAX_TREE)
+    return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 and tree_nodes in 1..64");
+  const int e = mlav::launch_tree_accept(tree_parents, draft_tokens, target_tokens, root_targets, batch,
+                                         tree_nodes, accept_len, accept_path, bonus_token, stream);
+  if (e != 0) return fail(MLA_ERR_HIP, "tree acceptance launch failed (hipError " + std::to_string(e) + ")");
   return MLA_OK;
 }
 

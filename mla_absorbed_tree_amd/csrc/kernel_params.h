@@ -42,5 +42,8 @@ int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks,
 int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream);
 int launch_tree_masks(const int32_t* parents, int32_t batch, int32_t tree_nodes, uint64_t* masks,
                       void* stream);
+int launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target,
+                       const int32_t* root_target, int32_t batch, int32_t T, int32_t* accept_len,
+                       int32_t* accept_path, int32_t* bonus, void* stream);
 
 }  // namespace mlav

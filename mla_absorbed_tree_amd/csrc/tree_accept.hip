@@ -1,0 +1,71 @@
+// Greedy token acceptance over a verified draft tree: one 64-lane wave per
+// sequence, one tree node per lane. Acceptance of a node is the AND of a local
+// test (its draft token equals the target's token after its parent) over its
+// ancestor-or-self set, which the shared pointer-doubling mask gives directly:
+// accepted(t) = (anc(t) & ~ok) == 0.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "wave_tree.h"
+
+namespace mlav {
+
+__global__ void __launch_bounds__(64) mla_tree_accept_kernel(const int32_t* __restrict__ parents,
+                                                             const int32_t* __restrict__ draft,
+                                                             const int32_t* __restrict__ target,
+                                                             const int32_t* __restrict__ root_target, int T,
+                                                             int32_t* __restrict__ accept_len,
+                                                             int32_t* __restrict__ accept_path,
+                                                             int32_t* __restrict__ bonus) {
+  const int b = blockIdx.x;
+  const int lane = lane_id();
+  const bool live = lane < T;
+  const int64_t base = (int64_t)b * T;
+  const uint64_t anc = wave_tree_mask(parents + base, T);
+  const int root_tok = root_target[b];
+  bool ok = false;
+  if (live && anc != 0) {
+    const int par = parents[base + lane];
+    const int want = par < 0 ? root_tok : target[base + par];
+    ok = draft[base + lane] == want;
+  }
+  const uint64_t ok_mask = __ballot(ok);
+  const bool accepted = live && anc != 0 && (anc & ~ok_mask) == 0;
+  const int depth = __popcll(anc);
+  // Deepest accepted node, smallest index among equals: maximise
+  // depth * 64 + (63 - lane) over the wave.
+  int key = accepted ? depth * 64 + (63 - lane) : -1;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) key = max(key, shfl_i32(key, lane ^ off));
+  if (live) accept_path[base + lane] = -1;
+  if (key < 0) {
+    if (lane == 0) {
+      accept_len[b] = 0;
+      bonus[b] = root_tok;
+    }
+    return;
+  }
+  const int best = 63 - (key & 63), len = key >> 6;
+  const uint64_t path = node_mask(anc, best);
+  // Every node on the path writes itself at its own depth (the path holds one
+  // node per depth). The -1 fill above comes first in program order on the
+  // same lane, or on another lane whose slot this lane does not write.
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (live && ((path >> lane) & 1ull)) accept_path[base + depth - 1] = lane;
+  if (lane == 0) {
+    accept_len[b] = len;
+    bonus[b] = target[base + best];
+  }
+}
+
+int launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target,
+                       const int32_t* root_target, int32_t batch, int32_t T, int32_t* accept_len,
+                       int32_t* accept_path, int32_t* bonus, void* stream) {
+  hipLaunchKernelGGL(mla_tree_accept_kernel, dim3((unsigned)batch), dim3(64), 0, (hipStream_t)stream, parents,
+                     draft, target, root_target, (int)T, accept_len, accept_path, bonus);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mlav

@@ -37,6 +37,7 @@
 #include <cstdint>
 
 #include "kernel_params.h"
+#include "wave_tree.h"
 #include "plan.h"
 
 namespace mlav {
@@ -64,15 +65,9 @@ constexpr float kLn2 = 0.693147180559945309f;
 // summed over millions of keys.
 constexpr float kOverflowSlack = 64.f;
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-__device__ __forceinline__ int shfl_i32(int v, int src_lane) {
-  return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
-}
 __device__ __forceinline__ float shfl_f32(float v, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
 }
-// Value held by the lane in the other half of the wave (lane ^ 32).
 // Value of lane i ^ 32: one v_permlane32_swap (lanes i and i + 32 trade
 // registers; measured layout: lane i < 32 finds lane i + 32's first operand
 // in the second result, lane i + 32 finds lane i's second operand in the
@@ -98,43 +93,6 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// Ancestor-or-self mask of tree node `lane` (lanes >= T return 0), by pointer
-// doubling over the parent array: after r rounds a node has OR-ed the masks of
-// the 2^r nearest nodes on its root path; 6 rounds cover a 64-deep chain.
-// A node whose root path holds an invalid parent (>= its node, or < -1) gets 0.
-// Every lane of the wave must execute this.
-__device__ __forceinline__ uint64_t wave_tree_mask(const int32_t* __restrict__ parents_b, int T) {
-  const int lane = lane_id();
-  const bool live = lane < T;
-  const int par = live ? parents_b[lane] : -1;
-  int bad = (live && (par < -1 || par >= lane)) ? 1 : 0;
-  int ptr = bad ? -1 : par;
-  uint32_t lo = (live && lane < 32) ? (1u << lane) : 0u;
-  uint32_t hi = (live && lane >= 32) ? (1u << (lane - 32)) : 0u;
-#pragma unroll
-  for (int r = 0; r < 6; ++r) {
-    const int src = ptr >= 0 ? ptr : lane;
-    const uint32_t slo = (uint32_t)shfl_i32((int)lo, src);
-    const uint32_t shi = (uint32_t)shfl_i32((int)hi, src);
-    const int sptr = shfl_i32(ptr, src);
-    const int sbad = shfl_i32(bad, src);
-    if (ptr >= 0) {
-      lo |= slo;
-      hi |= shi;
-      bad |= sbad;
-      ptr = sptr;
-    }
-  }
-  return bad ? 0ull : ((uint64_t)hi << 32) | lo;
-}
-
-// Mask of `node` fetched from the lane that built it.
-__device__ __forceinline__ uint64_t node_mask(uint64_t tmask, int node) {
-  const uint32_t lo = (uint32_t)shfl_i32((int)(uint32_t)tmask, node);
-  const uint32_t hi = (uint32_t)shfl_i32((int)(uint32_t)(tmask >> 32), node);
-  return ((uint64_t)hi << 32) | lo;
 }
 
 __global__ void __launch_bounds__(64) mla_tree_masks_kernel(const int32_t* __restrict__ parents, int T,

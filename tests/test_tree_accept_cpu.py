@@ -1,0 +1,95 @@
+"""Token acceptance on the CPU: the oracle against hand-worked cases, the
+linear (chain) special case, and a path-enumeration brute force; plus the
+C-ABI argument checks (no device work)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from gen import make_accept_tokens, make_tree_parents
+from oracle import tree_accept
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_hand_worked_cases():
+    g = json.load(open(os.path.join(HERE, "golden", "tree_accept_small.json")))
+    for c in g["cases"]:
+        got = tree_accept(np.array(c["parents"]), np.array(c["draft"]), np.array(c["target"]),
+                          c["root_target"])
+        assert got == (c["accept_len"], c["path"], c["bonus"]), c["name"]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_chain_is_linear_speculative_acceptance(seed):
+    """On a chain the tree rule is ordinary linear speculative decoding: accept
+    the longest draft prefix that matches the target's tokens shifted by one."""
+    rng = np.random.default_rng(seed)
+    T = 40
+    parents = np.arange(-1, T - 1)
+    draft, target, root = make_accept_tokens(rng, parents, vocab=3, p_match=0.9)
+    want = np.concatenate([[root], target[:-1]])     # token the target emits before each position
+    n = 0
+    while n < T and draft[n] == want[n]:
+        n += 1
+    got = tree_accept(parents, draft, target, root)
+    assert got == (n, list(range(n)), int(target[n - 1]) if n else root)
+
+
+def _brute_force(parents, draft, target, root):
+    """Every node's root path by walking parent pointers; a path is accepted
+    when every step matches; keep the deepest, smallest index first."""
+    best = (0, [], int(root))
+    for t in range(len(parents)):
+        path, u, ok = [], t, True
+        while u >= 0:
+            p = int(parents[u])
+            if p < -1 or p >= u:
+                ok = False
+                break
+            path.append(u)
+            u = p
+        if not ok:
+            continue
+        path.reverse()
+        prev_tok = root
+        for u in path:
+            if draft[u] != prev_tok:
+                ok = False
+                break
+            prev_tok = target[u]
+        if ok and len(path) > best[0]:
+            best = (len(path), path, int(target[t]))
+    return best
+
+
+@pytest.mark.parametrize("kind", ["uniform", "bounded", "chain"])
+def test_brute_force_agrees(kind):
+    rng = np.random.default_rng({"uniform": 10, "bounded": 11, "chain": 12}[kind])
+    for T in (1, 2, 5, 17, 64):
+        for _ in range(20):
+            parents = make_tree_parents(rng, T, kind)
+            if T > 3 and rng.random() < 0.3:      # plant an invalid parent
+                k = int(rng.integers(1, T))
+                parents = parents.copy()
+                parents[k] = k + int(rng.integers(0, 3))
+            draft, target, root = make_accept_tokens(rng, parents, vocab=3, p_match=0.8)
+            assert tree_accept(parents, draft, target, root) == _brute_force(parents, draft, target, root)
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mla_absorbed_tree_amd import binding
+    return binding
+
+
+def test_capi_argument_checks(B):
+    fake = 1 << 20  # never dereferenced: every call below fails validation first
+    args = dict(tree_parents=fake, draft_tokens=fake, target_tokens=fake, root_targets=fake, batch=2,
+                tree_nodes=16, accept_len=fake, accept_path=fake, bonus_token=fake, stream=0)
+    for over in (dict(batch=0), dict(tree_nodes=0), dict(tree_nodes=65), dict(draft_tokens=0),
+                 dict(accept_path=0)):
+        with pytest.raises(B.MlaVerifyError) as e:
+            B.mla_tree_accept(**{**args, **over})
+        assert e.value.status == B.MLA_ERR_INVALID_ARG, over

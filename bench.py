@@ -7,7 +7,8 @@ of synthetic inputs that already sit in HBM. The primary workload is the
 32k-prefix batch (B=4, H=64, P=32768, T=64, bf16); the 200k-prefix workload
 (B=1, H=64, P=200000, T=32, 256 splits) is reported in "also", and the KV
 compaction of the paged workload's 600k-slot pool (its kernel's HBM rate, and
-the verify step on the scattered against the compacted pool) in "kv_compact".
+the verify step on the scattered against the compacted pool) in "kv_compact",
+and the token-acceptance launch that follows a verify step in "tree_accept".
 
 Prints ONE JSON line. `value` is KV tokens/s (sum of N_b per step / step time);
 `roofline` describes the attention kernel (algorithmic FLOPs per launch over
@@ -196,6 +197,35 @@ def bench_kv_compact(steps, warmup, name="b8_h64_paged600k_t16_bf16"):
             "verify_step_ms_scattered": t_scattered, "verify_step_ms_compacted": t_compacted}
 
 
+def bench_tree_accept(steps, warmup, batch=8, tree_nodes=16, seed=7):
+    """Token acceptance after the verify step (one launch per decode step) on
+    synthetic draft/target tokens: its average launch time."""
+    import torch
+    from gen import make_accept_tokens, make_tree_parents
+    from mla_absorbed_tree_amd import binding as B
+
+    rng = np.random.default_rng(seed)
+    parents = np.stack([make_tree_parents(rng, tree_nodes, "uniform") for _ in range(batch)])
+    toks = [make_accept_tokens(rng, parents[b]) for b in range(batch)]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    args = (dev(parents), dev(np.stack([t[0] for t in toks])), dev(np.stack([t[1] for t in toks])),
+            dev(np.array([t[2] for t in toks])), batch, tree_nodes,
+            torch.empty(batch, dtype=torch.int32, device="cuda"),
+            torch.empty((batch, tree_nodes), dtype=torch.int32, device="cuda"),
+            torch.empty(batch, dtype=torch.int32, device="cuda"))
+    for _ in range(warmup):
+        B.mla_tree_accept(*args)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        B.mla_tree_accept(*args)
+    ev[1].record()
+    torch.cuda.synchronize()
+    return {"batch": batch, "tree_nodes": tree_nodes, "us_per_launch": ev[0].elapsed_time(ev[1]) / steps * 1e3,
+            "bound": "launch latency (one wave per sequence)"}
+
+
 def kernel_source_digest():
     """sha256 of the kernel source with its // comments and blank lines removed:
     it changes with the code, not with its comments."""
@@ -286,9 +316,10 @@ def main():
         r2, _ = bench_workload(ALSO, a.steps, a.warmup)
         also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "hbm_gbps", "hbm_frac",
                                         "mfma_frac", "kernels_ms", "roofline", "config", "plan")})
-    compact = None
+    compact = accept = None
     if not a.no_also and not a.no_compact:
         compact = bench_kv_compact(a.steps, a.warmup)
+        accept = bench_tree_accept(a.steps, a.warmup)
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the float64 oracle on a bounded sample")
@@ -317,6 +348,7 @@ def main():
         "cpu_baseline": cpu,
         "also": also,
         "kv_compact": compact,
+        "tree_accept": accept,
     }
     print(json.dumps(line), flush=True)
 

@@ -29,6 +29,8 @@ class VerifyConfig:
     dtype: str                       # "f32" or "bf16" (q, kv_c, k_pe share it)
     prefix: Optional[int] = None     # fixed prefix length for every sequence
     prefix_range: Optional[Tuple[int, int]] = None  # inclusive uniform range
+    tree_range: Optional[Tuple[int, int]] = None  # per-sequence tree sizes, inclusive uniform
+                                     # range (packed layout); tree_nodes is then the largest
     tree_kind: str = "uniform"       # "uniform": parent of i ~ U{0..i-1}; "bounded"
     max_depth: int = 8               # bounded trees only (node 0 has depth 1)
     max_branch: int = 4              # bounded trees only
@@ -44,6 +46,7 @@ class VerifyConfig:
 
     @property
     def rows(self) -> int:
+        """Query rows of a uniform-tree workload (ragged: see VerifyInputs.rows)."""
         return self.batch * self.tree_nodes * self.heads
 
 

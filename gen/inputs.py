@@ -1,12 +1,15 @@
 """Seeded input generator for the tree-verify workloads.
 
 Draw order, fixed so that a workload is reproducible from its seed:
-prefix lengths (only when they are random), tree parents (sequence by
-sequence), q_nope, q_pe, kv_c, k_pe, then the slot permutation (paged layout
-only).
+prefix lengths (only when they are random), tree sizes (only when they are
+random), tree parents (sequence by sequence), q_nope, q_pe, kv_c, k_pe, then
+the slot permutation (paged layout only).
 
 Layout of what is produced (row-major numpy arrays):
+  tree_indptr int32 [B+1] sequence b owns tree nodes tree_indptr[b]..tree_indptr[b+1]-1
+                          (b*T for equal tree sizes)
   q_nope   [B*T, H, Dl]   absorbed no-RoPE query, row (b*T + t), head h
+                          (packed trees: row tree_indptr[b] + t)
   q_pe     [B*T, H, Dr]   RoPE part of the query
   kv_c     [slots, Dl]    latent cache, one row per cache slot
   k_pe     [slots, Dr]    decoupled RoPE key, one row per cache slot
@@ -14,7 +17,7 @@ Layout of what is produced (row-major numpy arrays):
   kv_indices int32 [sum N_b]  slot of logical position j (prefix first, then the
                           T tree nodes in node order; page_size = 1)
   parents  int32 [B, T]   parent node of each tree node; -1 = child of the last
-                          prefix token; parent[t] < t
+                          prefix token; parent[t] < t (packed trees: [sum T_b])
 Floating arrays are float32. For bf16 workloads every value is already rounded
 to bf16 (round-to-nearest-even), so widening to float64 or narrowing to bf16 is
 exact on either side.
@@ -41,6 +44,15 @@ class VerifyInputs:
     parents: np.ndarray
     prefix_lens: np.ndarray
     scale: float
+    tree_indptr: Optional[np.ndarray] = None
+
+    @property
+    def tree_lens(self) -> np.ndarray:
+        return np.diff(self.tree_indptr).astype(np.int64)
+
+    @property
+    def rows(self) -> int:
+        return int(self.tree_indptr[-1]) * self.cfg.heads
 
     @property
     def kv_lens(self) -> np.ndarray:
@@ -109,12 +121,15 @@ def _normal(rng: np.random.Generator, shape, std: float, bf16: bool) -> np.ndarr
 
 
 def make_inputs(cfg: VerifyConfig, *, poison_unused: bool = False,
-                prefix_lens: Optional[np.ndarray] = None) -> VerifyInputs:
+                prefix_lens: Optional[np.ndarray] = None,
+                tree_lens: Optional[np.ndarray] = None) -> VerifyInputs:
     """Draw the inputs of workload ``cfg`` from ``default_rng(cfg.seed)``.
 
     ``poison_unused`` fills cache slots that no sequence references with NaN
     (paged layout; the draws are unchanged). ``prefix_lens`` overrides the
-    prefix lengths (then no length draw happens).
+    prefix lengths (then no length draw happens). ``tree_lens`` (or
+    ``cfg.tree_range``) gives every sequence its own tree size and packs the
+    trees; each size must lie in 0..cfg.tree_nodes.
     """
     rng = np.random.default_rng(cfg.seed)
     B, T, H, Dl, Dr = cfg.batch, cfg.tree_nodes, cfg.heads, cfg.d_latent, cfg.d_rope
@@ -130,13 +145,30 @@ def make_inputs(cfg: VerifyConfig, *, poison_unused: bool = False,
         P = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int64)
     else:
         P = np.full(B, int(cfg.prefix), dtype=np.int64)
-    N = P + T
+    ragged = tree_lens is not None or cfg.tree_range is not None
+    if tree_lens is not None:
+        Tb = np.asarray(tree_lens, dtype=np.int64)
+        assert Tb.shape == (B,)
+    elif cfg.tree_range is not None:
+        lo, hi = cfg.tree_range
+        Tb = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int64)
+    else:
+        Tb = np.full(B, T, dtype=np.int64)
+    if (Tb < 0).any() or (Tb > T).any():
+        raise ValueError("tree sizes must lie in 0..%d" % T)
+    N = P + Tb
+    tree_indptr = np.concatenate([[0], np.cumsum(Tb)]).astype(np.int32)
 
-    parents = np.stack([make_tree_parents(rng, T, cfg.tree_kind, cfg.max_depth, cfg.max_branch)
-                        for _ in range(B)]) if B else np.zeros((0, T), np.int32)
+    trees = [make_tree_parents(rng, int(Tb[b]), cfg.tree_kind, cfg.max_depth, cfg.max_branch)
+             for b in range(B)]
+    if ragged:
+        parents = np.concatenate(trees) if B else np.zeros(0, np.int32)
+    else:
+        parents = np.stack(trees) if B else np.zeros((0, T), np.int32)
+    nodes = int(tree_indptr[-1])
 
-    q_nope = _normal(rng, (B * T, H, Dl), cfg.q_std, bf16)
-    q_pe = _normal(rng, (B * T, H, Dr), cfg.q_std, bf16)
+    q_nope = _normal(rng, (nodes, H, Dl), cfg.q_std, bf16)
+    q_pe = _normal(rng, (nodes, H, Dr), cfg.q_std, bf16)
 
     total = int(N.sum())
     slots = cfg.pool_slots if cfg.layout == "paged" else total
@@ -162,7 +194,7 @@ def make_inputs(cfg: VerifyConfig, *, poison_unused: bool = False,
     return VerifyInputs(cfg=cfg, q_nope=q_nope, q_pe=q_pe, kv_c=kv_c, k_pe=k_pe,
                         kv_indptr=indptr.astype(np.int32), kv_indices=indices,
                         parents=parents.astype(np.int32), prefix_lens=P,
-                        scale=float(cfg.scale))
+                        scale=float(cfg.scale), tree_indptr=tree_indptr)
 
 
 def make_accept_tokens(rng: np.random.Generator, parents: np.ndarray, vocab: int = 4,

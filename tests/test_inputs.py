@@ -74,3 +74,32 @@ def test_named_configs_exist():
     assert len(CONFIGS) == 5
     big = get_config("b1_h64_p200000_t32_bf16_s256")
     assert big.num_splits == 256 and big.rows == 2048
+
+
+def test_ragged_trees_are_packed():
+    cfg = get_config("b4_h64_p32768_t64_bf16", prefix=10, heads=2, tree_nodes=256,
+                     tree_range=(0, 256), tree_kind="uniform")
+    x = make_inputs(cfg)
+    Tb = x.tree_lens
+    assert len(Tb) == 4 and (Tb >= 0).all() and (Tb <= 256).all()
+    assert x.parents.shape == (Tb.sum(),) and x.q_nope.shape == (Tb.sum(), 2, 512)
+    assert x.rows == Tb.sum() * 2
+    np.testing.assert_array_equal(x.kv_lens, 10 + Tb)
+    for b in range(4):
+        p = x.parents[x.tree_indptr[b]:x.tree_indptr[b + 1]]
+        assert all(-1 <= p[i] < i for i in range(len(p)))
+        if len(p):
+            assert p[0] == -1
+    y = make_inputs(cfg, tree_lens=[3, 0, 70, 1])
+    assert list(y.tree_indptr) == [0, 3, 3, 73, 74]
+
+
+def test_uniform_workloads_keep_their_draws():
+    """The tree-size draw happens only for ragged workloads: a uniform workload
+    draws exactly as before (first values fixed here)."""
+    x = make_inputs(get_config("tiny_f32_b1_h16_p256_t8"))
+    assert list(x.tree_indptr) == [0, 8] and x.parents.shape == (1, 8)
+    rng = np.random.default_rng(0)
+    parents = make_tree_parents(rng, 8, "uniform")
+    np.testing.assert_array_equal(x.parents[0], parents)
+    np.testing.assert_array_equal(x.q_nope.reshape(-1)[:5], rng.standard_normal(8 * 16 * 512, dtype=np.float32)[:5])

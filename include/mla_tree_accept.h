@@ -36,13 +36,16 @@
 extern "C" {
 #endif
 
+/* Largest tree the acceptance kernel handles (one node per lane of a wave). */
+#define MLA_TREE_ACCEPT_MAX_TREE 64
+
 /*
  *   tree_parents  device int32 [batch, T], as for mla_verify_run
  *   draft_tokens  device int32 [batch, T]
  *   target_tokens device int32 [batch, T]: target's greedy token after node t
  *   root_targets  device int32 [batch]: target's token after the last prefix
  *                 token of sequence b
- *   batch >= 1, T = tree_nodes in 1..MLA_VERIFY_MAX_TREE
+ *   batch >= 1, T = tree_nodes in 1..MLA_TREE_ACCEPT_MAX_TREE
  *   accept_len    device int32 [batch], written
  *   accept_path   device int32 [batch, T], written
  *   bonus_token   device int32 [batch], written

@@ -55,21 +55,29 @@ typedef struct mla_verify_plan_s* mla_verify_plan_t;
 typedef struct {
   int32_t batch;            /* B sequences, 1..MLA_VERIFY_MAX_BATCH */
   int32_t num_heads;        /* H >= 1 */
-  int32_t tree_nodes;       /* T nodes per sequence, 1..64 (one 64-bit mask word) */
+  int32_t tree_nodes;       /* T nodes per sequence, 1..MLA_VERIFY_MAX_TREE; with
+                               tree_len_host, an upper bound of every T_b */
   int32_t d_latent;         /* must be 512 */
   int32_t d_rope;           /* must be 64 */
   int32_t dtype;            /* mla_dtype of q_nope, q_pe, kv_c and k_pe; out/lse are fp32 */
-  const int32_t* kv_len_host; /* host [batch]: N_b = P_b + T tokens of sequence b (>= T).
+  const int32_t* kv_len_host; /* host [batch]: N_b = P_b + T_b tokens of sequence b (>= T_b).
                                  Read during the call only; sizes the split schedule
                                  (the lengths a run sees may differ, see mla_verify_run). */
   int32_t num_splits;       /* 0 = planner's choice; > 0 forces that many KV splits
                                for every sequence (capped at its number of key tiles) */
   int64_t kv_c_row_stride;  /* elements between consecutive kv_c slots (>= 512, multiple of 8) */
   int64_t k_pe_row_stride;  /* elements between consecutive k_pe slots (>= 64, multiple of 8) */
+  const int32_t* tree_len_host; /* host [batch]: T_b, the tree nodes of sequence b, each in
+                                   0..tree_nodes (0: the sequence has no query this step),
+                                   or NULL: every sequence has tree_nodes nodes. Read during
+                                   the call only; fixed for the plan's runs. The pages ask for
+                                   trees of arbitrary size ["Ground Truth in Silicon" page,
+                                   "Input Knowledge Required", item 3]. */
 } mla_verify_problem;
 
 #define MLA_VERIFY_MAX_BATCH 256
-#define MLA_VERIFY_MAX_TREE 64
+/* Ancestor masks are four 64-bit words per node. */
+#define MLA_VERIFY_MAX_TREE 256
 
 typedef struct {
   int32_t total_splits;     /* sum over sequences of the KV splits */
@@ -97,32 +105,38 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
 /*
  * Tree-verify attention of one batch (device work on `stream`, asynchronous).
  *
- *   q_nope      device [batch*T, H, 512] of dtype, row-major; row (b*T + t), head h
- *   q_pe        device [batch*T, H, 64]  of dtype, row-major
+ * Trees are packed: with node_off[b] = T_0 + ... + T_{b-1} (b*T when
+ * tree_len_host is NULL), tree node t of sequence b is packed node
+ * node_off[b] + t, and nodes = node_off[batch] in all.
+ *   q_nope      device [nodes, H, 512] of dtype, row-major; row node_off[b] + t, head h
+ *   q_pe        device [nodes, H, 64]  of dtype, row-major
  *   kv_c        device, slot s at kv_c + s*kv_c_row_stride, 512 elements
  *   k_pe        device, slot s at k_pe + s*k_pe_row_stride, 64 elements
  *               (kv_c and k_pe may interleave inside one 576-wide buffer)
  *   kv_indptr   device int32 [batch+1]; kv_indptr[0] = 0 and
- *               N_b = kv_indptr[b+1] - kv_indptr[b] >= T.  N_b may differ from
+ *               N_b = kv_indptr[b+1] - kv_indptr[b] >= T_b.  N_b may differ from
  *               the plan's kv_len_host[b] (one plan, or one captured graph,
  *               serves decode steps whose lengths change on the device): each
  *               sequence keeps the plan's split count over its actual length,
  *               and a split left without keys contributes nothing.
  *   kv_indices  device int32 [kv_indptr[batch]]: slot of logical position j of
  *               sequence b at kv_indices[kv_indptr[b] + j] (page_size = 1).
- *               Positions 0..P_b-1 are the prefix, P_b..P_b+T-1 the tree nodes.
- *   tree_parents device int32 [batch, T]: parent node of each node, -1 = child
- *               of the last prefix token; parent[t] < t.  A node whose parent
- *               chain is invalid gets NaN output rows and lse.
+ *               Positions 0..P_b-1 are the prefix, P_b..P_b+T_b-1 the tree nodes.
+ *   tree_parents device int32 [nodes]: parent of packed node node_off[b] + t as
+ *               a node index of the same tree, -1 = child of the last prefix
+ *               token; parent[t] < t.  A node whose parent chain is invalid gets
+ *               NaN output rows and lse.
  *   scale       softmax scale applied to the summed dot products; positive
  *               and finite (MLA_ERR_INVALID_ARG otherwise)
- *   out         device fp32 [batch*T, H, 512]
- *   lse         device fp32 [batch*T, H] (natural log) or NULL
+ *   out         device fp32 [nodes, H, 512]
+ *   lse         device fp32 [nodes, H] (natural log) or NULL
  *   workspace   device, >= workspace_bytes of the plan, 256-byte aligned.  Holds
  *               split partials between the two launches; concurrent runs need
  *               separate workspaces.
  * No allocation, no host synchronisation and no host reads of device data:
  * the call only enqueues kernels, so it can be captured in a HIP graph.
+ * A plan whose trees are all empty (nodes = 0) enqueues nothing; q_nope, q_pe,
+ * tree_parents, out and lse may then be NULL.
  */
 mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
                           const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
@@ -155,9 +169,11 @@ mla_status mla_verify_combine(mla_verify_plan_t plan, float* out, float* lse, vo
 /*
  * Ancestor-or-self bitmask of every tree node (device work on `stream`).
  *   tree_parents device int32 [batch, tree_nodes], as in mla_verify_run
- *   masks        device uint64 [batch, tree_nodes]; bit u of masks[b*T + t] is
- *                set iff node u is t or an ancestor of t.  0 marks an invalid
- *                parent chain (parent >= node or < -1 somewhere on it).
+ *   tree_nodes   1..MLA_VERIFY_MAX_TREE; W = ceil(tree_nodes / 64) words per node
+ *   masks        device uint64 [batch, tree_nodes, W]; bit u % 64 of word u / 64
+ *                of node (b, t) is set iff node u is t or an ancestor of t.  All
+ *                words 0 mark an invalid parent chain (parent >= node or < -1
+ *                somewhere on it).
  * This is the mask mla_verify_run applies to the tree-tail keys.
  */
 mla_status mla_verify_tree_masks(const int32_t* tree_parents, int32_t batch, int32_t tree_nodes,

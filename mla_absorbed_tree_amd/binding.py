@@ -23,7 +23,8 @@ MLA_ERR_HIP = -4
 MLA_DTYPE_F32 = 0
 MLA_DTYPE_BF16 = 1
 MLA_VERIFY_MAX_BATCH = 256
-MLA_VERIFY_MAX_TREE = 64
+MLA_VERIFY_MAX_TREE = 256
+MLA_TREE_ACCEPT_MAX_TREE = 64
 
 # Symbols declared in include/*.h.
 EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
@@ -44,7 +45,8 @@ class mla_verify_problem(ctypes.Structure):
                 ("tree_nodes", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("d_rope", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("kv_len_host", ctypes.POINTER(ctypes.c_int32)), ("num_splits", ctypes.c_int32),
-                ("kv_c_row_stride", ctypes.c_int64), ("k_pe_row_stride", ctypes.c_int64)]
+                ("kv_c_row_stride", ctypes.c_int64), ("k_pe_row_stride", ctypes.c_int64),
+                ("tree_len_host", ctypes.POINTER(ctypes.c_int32))]
 
 
 class mla_verify_plan_info(ctypes.Structure):
@@ -127,12 +129,20 @@ def mla_verify_last_error() -> str:
 def mla_verify_plan(batch: int, num_heads: int, tree_nodes: int, dtype: int,
                     kv_len_host: Sequence[int], num_splits: int = 0,
                     kv_c_row_stride: int = 512, k_pe_row_stride: int = 64,
-                    d_latent: int = 512, d_rope: int = 64):
-    """Returns (plan handle, workspace bytes). Raises MlaVerifyError on a bad problem."""
+                    d_latent: int = 512, d_rope: int = 64,
+                    tree_len_host: Optional[Sequence[int]] = None):
+    """Returns (plan handle, workspace bytes). Raises MlaVerifyError on a bad problem.
+
+    tree_len_host: per-sequence tree sizes (packed trees), or None for
+    ``tree_nodes`` nodes in every sequence."""
+    i32p = ctypes.POINTER(ctypes.c_int32)
     lens = np.ascontiguousarray(np.asarray(kv_len_host, dtype=np.int32))
+    tlens = None if tree_len_host is None else \
+        np.ascontiguousarray(np.asarray(tree_len_host, dtype=np.int32))
     prob = mla_verify_problem(batch, num_heads, tree_nodes, d_latent, d_rope, dtype,
-                              lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), num_splits,
-                              kv_c_row_stride, k_pe_row_stride)
+                              lens.ctypes.data_as(i32p), num_splits,
+                              kv_c_row_stride, k_pe_row_stride,
+                              None if tlens is None else tlens.ctypes.data_as(i32p))
     plan = ctypes.c_void_p()
     ws = ctypes.c_size_t()
     _check(_lib.mla_verify_plan(ctypes.byref(prob), ctypes.byref(plan), ctypes.byref(ws)))
@@ -183,6 +193,7 @@ def mla_verify_combine(plan, out, lse, workspace, workspace_bytes: Optional[int]
 
 
 def mla_verify_tree_masks(tree_parents, batch: int, tree_nodes: int, masks, stream=None) -> None:
+    """masks: uint64-sized device buffer [batch, tree_nodes, ceil(tree_nodes / 64)]."""
     _check(_lib.mla_verify_tree_masks(_ptr(tree_parents), int(batch), int(tree_nodes), _ptr(masks),
                                       _stream_handle(stream)))
 

@@ -75,9 +75,12 @@ mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
                    void* workspace, size_t workspace_bytes, bool need_inputs, mlav::VerifyArgs& a) {
   if (!plan) return fail(MLA_ERR_INVALID_ARG, "plan is NULL");
   const mlav::Plan& p = plan->plan;
-  if (need_inputs && (!q_nope || !q_pe || !kv_c || !k_pe || !kv_indptr || !kv_indices || !tree_parents))
+  // A batch without any tree node has no query rows: its q, parent and output
+  // buffers are empty and may be NULL.
+  const bool rows = p.node_offset[p.batch] > 0;
+  if (need_inputs && (!kv_c || !k_pe || !kv_indptr || !kv_indices || (rows && (!q_nope || !q_pe || !tree_parents))))
     return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
-  if (!out) return fail(MLA_ERR_INVALID_ARG, "out is NULL");
+  if (!out && rows) return fail(MLA_ERR_INVALID_ARG, "out is NULL");
   if (need_inputs && (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_c) || !aligned16(k_pe)))
     return fail(MLA_ERR_INVALID_ARG, "q_nope, q_pe, kv_c and k_pe must be 16-byte aligned");
   if (!aligned16(out)) return fail(MLA_ERR_INVALID_ARG, "out must be 16-byte aligned");
@@ -107,14 +110,14 @@ mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.batch = p.batch;
   a.heads = p.heads;
-  a.tree_nodes = p.tree_nodes;
-  a.rows_per_seq = p.rows_per_seq;
+  a.max_rows_per_seq = p.max_rows_per_seq;
   a.part_rows = p.row_blocks * p.rows_per_block;
   a.row_blocks = p.row_blocks;
   a.total_splits = p.total_splits;
   for (int b = 0; b <= p.batch; ++b) a.split_offset[b] = p.split_offset[b];
   a.group = p.group;
   for (int b = 0; b <= p.batch; ++b) a.group_offset[b] = p.group_offset[b];
+  for (int b = 0; b <= p.batch; ++b) a.node_offset[b] = p.node_offset[b];
   return MLA_OK;
 }
 
@@ -178,7 +181,8 @@ mla_status mla_verify_tree_masks(const int32_t* tree_parents, int32_t batch, int
   g_last_error.clear();
   if (!tree_parents || !masks) return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
   if (batch < 1 || tree_nodes < 1 || tree_nodes > MLA_VERIFY_MAX_TREE)
-    return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 and tree_nodes in 1..64");
+    return fail(MLA_ERR_INVALID_ARG,
+                "batch must be >= 1 and tree_nodes in 1.." + std::to_string(MLA_VERIFY_MAX_TREE));
   const int e = mlav::launch_tree_masks(tree_parents, batch, tree_nodes, masks, stream);
   if (e != 0) return fail(MLA_ERR_HIP, "tree mask launch failed (hipError " + std::to_string(e) + ")");
   return MLA_OK;
@@ -236,8 +240,9 @@ mla_status mla_tree_accept(const int32_t* tree_parents, const int32_t* draft_tok
   if (!tree_parents || !draft_tokens || !target_tokens || !root_targets || !accept_len || !accept_path ||
       !bonus_token)
     return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
-  if (batch < 1 || tree_nodes < 1 || tree_nodes > MLA_VERIFY_MAX_TREE)
-    return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 and tree_nodes in 1..64");
+  if (batch < 1 || tree_nodes < 1 || tree_nodes > MLA_TREE_ACCEPT_MAX_TREE)
+    return fail(MLA_ERR_INVALID_ARG,
+                "batch must be >= 1 and tree_nodes in 1.." + std::to_string(MLA_TREE_ACCEPT_MAX_TREE));
   const int e = mlav::launch_tree_accept(tree_parents, draft_tokens, target_tokens, root_targets, batch,
                                          tree_nodes, accept_len, accept_path, bonus_token, stream);
   if (e != 0) return fail(MLA_ERR_HIP, "tree acceptance launch failed (hipError " + std::to_string(e) + ")");

@@ -7,19 +7,22 @@
 
 namespace mlav {
 
+// Trees are packed: sequence b owns tree nodes node_offset[b] ..
+// node_offset[b+1]-1 (b*T when every tree has T nodes), and query row
+// (node_offset[b] + t) * H + h.
 struct VerifyArgs {
-  const void* q_nope;          // [B*T, H, 512]
-  const void* q_pe;            // [B*T, H, 64]
+  const void* q_nope;          // [nodes, H, 512]
+  const void* q_pe;            // [nodes, H, 64]
   const void* kv_c;            // slot s at kv_c + s * kv_c_stride
   const void* k_pe;            // slot s at k_pe + s * k_pe_stride
   const int32_t* kv_indptr;    // [B + 1]
   const int32_t* kv_indices;   // page table, page_size = 1
-  const int32_t* parents;      // [B, T]
-  float* out;                  // [B*T, H, 512]
-  float* lse;                  // [B*T, H] or nullptr
+  const int32_t* parents;      // [nodes], node indices local to the sequence
+  float* out;                  // [nodes, H, 512]
+  float* lse;                  // [nodes, H] or nullptr
   // Split partials [total_splits, part_rows, 512] (split launches only):
   // unnormalised O = sum of 2^(s - m) v, fp32 for fp32 problems, bf16 for
-  // bf16 problems. Rows past rows_per_seq are padding (never read).
+  // bf16 problems. Rows past a sequence's T_b * H are padding (never read).
   void* part_o;
   float* part_ml;              // [total_splits, part_rows, 2]  (m in log2 units, l)
   int64_t kv_c_stride;         // elements
@@ -27,21 +30,21 @@ struct VerifyArgs {
   float scale_log2;            // softmax scale * log2(e)
   int32_t batch;
   int32_t heads;
-  int32_t tree_nodes;
-  int32_t rows_per_seq;        // T * H
-  int32_t part_rows;           // row_blocks * rows per workgroup (>= rows_per_seq)
-  int32_t row_blocks;          // workgroups along the rows of one sequence
+  int32_t max_rows_per_seq;    // largest T_b * H
+  int32_t part_rows;           // row_blocks * rows per workgroup (>= max_rows_per_seq)
+  int32_t row_blocks;          // workgroups along the rows of the largest tree
   int32_t total_splits;
   int32_t split_offset[MLA_VERIFY_MAX_BATCH + 1];  // first global split of sequence b
   int32_t group;                                   // consecutive splits per workgroup
   int32_t group_offset[MLA_VERIFY_MAX_BATCH + 1];  // first split group of sequence b
+  int32_t node_offset[MLA_VERIFY_MAX_BATCH + 1];   // first tree node of sequence b
 };
 
 // Launchers (defined in the HIP translation unit). Return the launch error.
 int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks, void* stream);
 int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream);
 int launch_tree_masks(const int32_t* parents, int32_t batch, int32_t tree_nodes, uint64_t* masks,
-                      void* stream);
+                      void* stream);  // masks [batch, tree_nodes, ceil(tree_nodes / 64)]
 int launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target,
                        const int32_t* root_target, int32_t batch, int32_t T, int32_t* accept_len,
                        int32_t* accept_path, int32_t* bonus, void* stream);

@@ -31,6 +31,13 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
     err = fmt("tree_nodes %lld outside 1..%lld", p.tree_nodes, MLA_VERIFY_MAX_TREE);
     return p.tree_nodes > MLA_VERIFY_MAX_TREE ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
   }
+  if (p.tree_len_host) {
+    for (int b = 0; b < p.batch; ++b)
+      if (p.tree_len_host[b] < 0 || p.tree_len_host[b] > p.tree_nodes) {
+        err = fmt("tree_len_host[%lld] = %lld is outside 0..tree_nodes", b, p.tree_len_host[b]);
+        return MLA_ERR_INVALID_ARG;
+      }
+  }
   if (p.d_latent != kDl || p.d_rope != kDr) {
     err = fmt("d_latent/d_rope %lld/%lld: only 512/64 is supported", p.d_latent, p.d_rope);
     return MLA_ERR_UNSUPPORTED;
@@ -60,6 +67,10 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
     err = fmt("tree_nodes * num_heads = %lld is too large", rows_per_seq);
     return MLA_ERR_INVALID_ARG;
   }
+  std::vector<int32_t> tree_len(p.batch);
+  for (int b = 0; b < p.batch; ++b) tree_len[b] = p.tree_len_host ? p.tree_len_host[b] : p.tree_nodes;
+  int32_t max_tree = 0;
+  for (int b = 0; b < p.batch; ++b) max_tree = std::max(max_tree, tree_len[b]);
 
   plan = Plan();
   plan.batch = p.batch;
@@ -68,22 +79,33 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   plan.dtype = p.dtype;
   plan.kv_c_stride = p.kv_c_row_stride;
   plan.k_pe_stride = p.k_pe_row_stride;
-  plan.rows_per_seq = int32_t(rows_per_seq);
+  plan.max_rows_per_seq = max_tree * p.num_heads;
   plan.rows_per_block = p.dtype == MLA_DTYPE_BF16 ? kRowsPerBlockBf16 : kRowsPerBlockF32;
-  plan.row_blocks = (plan.rows_per_seq + plan.rows_per_block - 1) / plan.rows_per_block;
+  plan.row_blocks = (plan.max_rows_per_seq + plan.rows_per_block - 1) / plan.rows_per_block;
+  plan.tree_len = tree_len;
+  plan.node_offset.assign(p.batch + 1, 0);
+  for (int b = 0; b < p.batch; ++b) plan.node_offset[b + 1] = plan.node_offset[b] + tree_len[b];
+  if (int64_t(plan.node_offset[p.batch]) * p.num_heads > (int64_t(1) << 30)) {
+    err = "total tree nodes * num_heads is too large";
+    return MLA_ERR_INVALID_ARG;
+  }
 
+  // Work of a sequence: its key tiles times its row blocks (a sequence
+  // without tree nodes has none and gets no split).
   plan.kv_len.resize(p.batch);
-  int64_t total_tiles = 0;
-  std::vector<int64_t> tiles(p.batch);
+  std::vector<int64_t> tiles(p.batch), row_blocks(p.batch);
+  int64_t work = 0, busy_row_blocks = 0;
   for (int b = 0; b < p.batch; ++b) {
     const int32_t n = p.kv_len_host[b];
-    if (n < p.tree_nodes) {
-      err = fmt("kv_len_host[%lld] = %lld is smaller than tree_nodes", b, n);
+    if (n < tree_len[b]) {
+      err = fmt("kv_len_host[%lld] = %lld is smaller than the sequence's tree", b, n);
       return MLA_ERR_INVALID_ARG;
     }
     plan.kv_len[b] = n;
-    tiles[b] = (int64_t(n) + kKeysPerTile - 1) / kKeysPerTile;
-    total_tiles += tiles[b];
+    row_blocks[b] = (int64_t(tree_len[b]) * p.num_heads + plan.rows_per_block - 1) / plan.rows_per_block;
+    tiles[b] = row_blocks[b] > 0 ? (int64_t(n) + kKeysPerTile - 1) / kKeysPerTile : 0;
+    work += row_blocks[b] * tiles[b];
+    busy_row_blocks += tiles[b] > 0 ? row_blocks[b] : 0;
   }
 
   // Split schedule. Forced: S_b = min(num_splits, tiles_b). Automatic: pick a
@@ -96,13 +118,12 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
     for (int b = 0; b < p.batch; ++b)
       plan.splits[b] = int32_t(std::min<int64_t>(p.num_splits, tiles[b]));
   } else {
-    const int64_t work = int64_t(plan.row_blocks) * total_tiles;
-    if (int64_t(plan.row_blocks) * p.batch >= kComputeUnits) {
-      std::fill(plan.splits.begin(), plan.splits.end(), 1);
+    if (busy_row_blocks >= kComputeUnits) {
+      for (int b = 0; b < p.batch; ++b) plan.splits[b] = tiles[b] > 0 ? 1 : 0;
     } else {
       const int64_t chunk = std::max<int64_t>(kMinChunkTiles, (work + kComputeUnits - 1) / kComputeUnits);
       for (int b = 0; b < p.batch; ++b)
-        plan.splits[b] = int32_t(std::max<int64_t>(1, (tiles[b] + chunk - 1) / chunk));
+        plan.splits[b] = tiles[b] > 0 ? int32_t(std::max<int64_t>(1, (tiles[b] + chunk - 1) / chunk)) : 0;
     }
     // Every KV chunk runs on one XCD (its row blocks share that XCD's L2):
     // with fewer chunks than XCDs some XCDs would idle, so split the longest
@@ -113,7 +134,7 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
       if (total >= kXcds) break;
       int best = -1;
       for (int b = 0; b < p.batch; ++b) {
-        if (tiles[b] / (plan.splits[b] + 1) < kMinChunkTiles) continue;
+        if (tiles[b] == 0 || tiles[b] / (plan.splits[b] + 1) < kMinChunkTiles) continue;
         if (best < 0 || tiles[b] * plan.splits[best] > tiles[best] * plan.splits[b]) best = b;
       }
       if (best < 0) break;
@@ -132,9 +153,11 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   // workgroup runs several consecutive splits, aiming at about one workgroup
   // per compute unit. The bf16 kernel only (the fp32 kernel runs one split).
   plan.group = 1;
-  if (p.dtype == MLA_DTYPE_BF16)
-    plan.group = int32_t(std::max<int64_t>(
-        1, int64_t(plan.total_splits) * plan.row_blocks / kComputeUnits));
+  if (p.dtype == MLA_DTYPE_BF16) {
+    int64_t split_row_blocks = 0;
+    for (int b = 0; b < p.batch; ++b) split_row_blocks += int64_t(plan.splits[b]) * row_blocks[b];
+    plan.group = int32_t(std::max<int64_t>(1, split_row_blocks / kComputeUnits));
+  }
   plan.group = std::min(plan.group, std::max(1, plan.max_splits));
   plan.group_offset.assign(p.batch + 1, 0);
   for (int b = 0; b < p.batch; ++b)

@@ -23,9 +23,11 @@ constexpr int kComputeUnits = 256;
 struct Plan {
   int32_t batch = 0, heads = 0, tree_nodes = 0, dtype = 0;
   int64_t kv_c_stride = 0, k_pe_stride = 0;
-  int32_t rows_per_seq = 0;     // T * H
+  int32_t max_rows_per_seq = 0; // largest T_b * H
   int32_t rows_per_block = 0;
-  int32_t row_blocks = 0;       // ceil(rows_per_seq / rows_per_block)
+  int32_t row_blocks = 0;       // ceil(max_rows_per_seq / rows_per_block)
+  std::vector<int32_t> tree_len;     // T_b
+  std::vector<int32_t> node_offset;  // [batch + 1] prefix sums of T_b (packed trees)
   std::vector<int32_t> kv_len;  // N_b from the host copy
   std::vector<int32_t> splits;  // S_b
   std::vector<int32_t> split_offset;  // [batch + 1] prefix sums of S_b

@@ -95,11 +95,26 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
-__global__ void __launch_bounds__(64) mla_tree_masks_kernel(const int32_t* __restrict__ parents, int T,
-                                                            uint64_t* __restrict__ masks) {
+// Ancestor masks of sequence blockIdx.x's tree, masks[(b*T + t) * W + w] with
+// W = ceil(T / 64): the one-wave builder for T <= 64 (the first wave), the
+// workgroup builder above, as in the attention kernels.
+constexpr int kTreeMaskThreads = 256;
+__global__ void __launch_bounds__(kTreeMaskThreads) mla_tree_masks_kernel(const int32_t* __restrict__ parents,
+                                                                          int T, uint64_t* __restrict__ masks) {
+  __shared__ __attribute__((aligned(16))) char scratch[kTreeScratchBytes];
   const int b = blockIdx.x;
-  const uint64_t m = wave_tree_mask(parents + (int64_t)b * T, T);
-  if (lane_id() < T) masks[(int64_t)b * T + lane_id()] = m;
+  const int32_t* par = parents + (int64_t)b * T;
+  if (T <= 64) {
+    if (threadIdx.x >= 64) return;
+    const uint64_t m = wave_tree_mask(par, T);
+    if (lane_id() < T) masks[(int64_t)b * T + lane_id()] = m;
+    return;
+  }
+  const int W = (T + 63) >> 6;
+  block_tree_masks<kTreeMaskThreads>(par, T, scratch);
+  const uint64_t* msk = tree_scratch_masks(scratch);
+  for (int i = threadIdx.x; i < T * W; i += kTreeMaskThreads)
+    masks[(int64_t)b * T * W + i] = msk[(i / W) * kMaskWords + i % W];
 }
 
 // ---------------------------------------------------------------------------
@@ -112,6 +127,7 @@ __global__ void __launch_bounds__(64) mla_tree_masks_kernel(const int32_t* __res
 // ---------------------------------------------------------------------------
 struct BlockWork {
   int b, S, rb;
+  int T, rows, node0;         // tree nodes of the sequence, T * H, its first packed node
   int s, c;                   // current split: index within the sequence, global index
   int s_last;                 // one past the group's last split (within the sequence)
   int kv0, N, P, ntiles;
@@ -122,7 +138,10 @@ struct BlockWork {
 // First key tile of split s of a sequence with ntiles tiles and S splits.
 __device__ __forceinline__ int split_tile(int s, int ntiles, int S) { return (int)(((int64_t)s * ntiles) / S); }
 
-__device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w) {
+// Returns false for a workgroup with nothing to do: past the last split group,
+// or a row block past its sequence's T_b * H rows (row blocks are counted for
+// the largest tree; smaller trees leave the rest idle).
+__device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w, int rows_per_block) {
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int local = bid / kXcds;
@@ -136,13 +155,17 @@ __device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w) {
     else hi = mid - 1;
   }
   w.b = lo;
+  w.node0 = a.node_offset[w.b];
+  w.T = a.node_offset[w.b + 1] - w.node0;
+  w.rows = w.T * a.heads;
+  if (w.rb * rows_per_block >= w.rows) return false;
   w.S = a.split_offset[w.b + 1] - a.split_offset[w.b];
   w.s = (cg - a.group_offset[w.b]) * a.group;
   w.s_last = min(w.s + a.group, w.S);
   w.c = a.split_offset[w.b] + w.s;
   w.kv0 = a.kv_indptr[w.b];
   w.N = a.kv_indptr[w.b + 1] - w.kv0;
-  w.P = w.N - a.tree_nodes;
+  w.P = w.N - w.T;
   w.seq_ok = w.P >= 0;
   w.ntiles = w.seq_ok ? (w.N + kKeysPerTile - 1) / kKeysPerTile : 0;
   w.tile_begin = split_tile(w.s, w.ntiles, w.S);
@@ -152,16 +175,18 @@ __device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w) {
 
 // Masks and scales the 16 scores this lane holds in an S^T block and returns
 // the row max over the 32 keys. Register i holds key k0 + (i/4)*8 + 4*half +
-// i%4. Prefix keys are visible; tail key P+u iff bit u of anc; keys >= N are
-// padding.
+// i%4. Prefix keys are visible; tail key P+u iff node u is in the row's
+// ancestor mask, whose bits for the tile's keys k0..k0+31 are `win`
+// (mask_window at u0 = k0 - P); keys >= N are padding.
 __device__ __forceinline__ float mask_scale_max(float (&sv)[16], const f32x16_t& sacc, float scale_log2,
-                                                int k0, int half, int P, int N, uint64_t anc) {
+                                                int k0, int half, int P, int N, uint32_t win) {
   const bool no_mask = k0 + kKeysPerTile <= P;
+  const uint32_t hwin = win >> (4 * half);
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int j = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
-    const bool tail_bit = ((anc >> ((j - P) & 63)) & 1ull) != 0;
+    const bool tail_bit = ((hwin >> ((i >> 2) * 8 + (i & 3))) & 1u) != 0;
     const bool vis = no_mask | (j < P) | ((j < N) & tail_bit);
     sv[i] = vis ? sacc[i] * scale_log2 : -INFINITY;
     mx = fmaxf(mx, sv[i]);
@@ -191,7 +216,7 @@ constexpr int kPBytes = kRows * kKeysPerTile * 2;           // 8192 per tile, do
 constexpr int kIdxRing = 4;
 constexpr int kIdxLead = 3;
 constexpr int kIdxBytes = kIdxRing * kKeysPerTile * 4;      // 512
-constexpr int kAncBytes = kRows * 8;                          // ancestor mask of each row
+constexpr int kAncBytes = kRows * kMaskWords * 8;             // ancestor mask words of each row
 // The rope part of Q (64 features of each row) as each lane's four MFMA
 // operand fragments, [wave][fragment][lane] x 16 bytes.
 constexpr int kQpeBytes = kRows * kDr * 2;                     // 16384
@@ -207,6 +232,8 @@ constexpr int kPartialStores = 1 + 4 * 4 * 2;
 // block of 8 k_pe rows, one block of 8 page-table entries.
 constexpr int kVmemPerTile = 10;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
+// Trees above 64 nodes build their masks in the P buffers before first use.
+static_assert(kTreeScratchBytes <= 2 * kPBytes, "tree mask scratch");
 }  // namespace bf16k
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -387,8 +414,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   char* const qpe_lds = idx_ring + kIdxBytes + kAncBytes;
 
   BlockWork w;
-  if (!map_block(a, w)) return;
-  const int T = a.tree_nodes, H = a.heads;
+  if (!map_block(a, w, kRows)) return;
+  const int H = a.heads;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;  // uniform: keep it scalar
@@ -405,8 +432,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 
   // ---- QK role: this lane's query row (wave owns rows 32w..32w+31) ---------
   const int r_local = w.rb * kRows + wave * 32 + qcol;
-  const int r_eff = min(r_local, a.rows_per_seq - 1);
-  const int64_t grow = (int64_t)w.b * a.rows_per_seq + r_eff;
+  const int r_eff = min(r_local, w.rows - 1);
+  const int64_t grow = (int64_t)w.node0 * H + r_eff;
   bf16x8_t qreg[32];
   const char* const qpe_lane = qpe_lds + (wave * 4 * 64 + lane) * 16;
   {
@@ -418,21 +445,48 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     for (int kc = 0; kc < 4; ++kc)  // only this lane reads these back
       *(bf16x8_t*)(qpe_lane + kc * 64 * 16) = *(const bf16x8_t*)(qp + kc * 16);
   }
-  const uint64_t tmask = wave_tree_mask(a.parents + (int64_t)w.b * T, T);
   // This lane's ancestor mask waits in LDS (read by the few tiles that reach
-  // the tree tail and by the epilogue) instead of holding two registers
-  // through the tile loop. Only the QK owner (half 0) writes it; the first
-  // barrier of the pipeline orders the write before every read.
+  // the tree tail and by the epilogue) instead of holding registers through
+  // the tile loop. Only the QK owner (half 0) writes it; the first barrier of
+  // the pipeline orders the write before every read. Trees of up to 64 nodes
+  // take the one-wave builder; larger ones are built by the workgroup in the
+  // P buffers, which are first written after that barrier.
   {
-    const uint64_t anc = node_mask(tmask, r_eff / H);
-    if (half == 0) anc_lds[wave * 32 + qcol] = w.seq_ok ? anc : 0ull;
+    uint64_t* const dst = anc_lds + (wave * 32 + qcol) * kMaskWords;
+    if (w.T <= 64) {
+      const uint64_t tmask = wave_tree_mask(a.parents + w.node0, w.T);
+      const uint64_t anc = node_mask(tmask, r_eff / H);
+      if (half == 0) {
+        dst[0] = w.seq_ok ? anc : 0ull;
+#pragma unroll
+        for (int k = 1; k < kMaskWords; ++k) dst[k] = 0ull;
+      }
+    } else {
+      block_tree_masks<kThreads>(a.parents + w.node0, w.T, pbuf0);
+      const uint64_t* src = tree_scratch_masks(pbuf0) + (r_eff / H) * kMaskWords;
+      if (half == 0) {
+#pragma unroll
+        for (int k = 0; k < kMaskWords; ++k) dst[k] = w.seq_ok ? src[k] : 0ull;
+      }
+    }
   }
-  // Ancestor mask of this lane's row (0: no valid node), loaded afresh so that
-  // the value is not carried through the loop in registers.
-  auto row_anc = [&]() {
+  // Mask bits of this lane's row for tail nodes u0..u0+31 (mask_window),
+  // loaded afresh so that nothing is carried through the loop in registers.
+  auto row_window = [&](int u0) {
     int i = wave * 32 + qcol;
     asm volatile("" : "+v"(i));
-    return anc_lds[i];
+    const int w0 = min(max(u0, 0) >> 6, kMaskWords - 1);
+    const uint64_t* m = anc_lds + i * kMaskWords;
+    return mask_window(u0, m[w0], w0 + 1 < kMaskWords ? m[w0 + 1] : 0ull);
+  };
+  // Whether this lane's row belongs to a valid node (its mask is not empty).
+  auto row_valid = [&]() {
+    int i = wave * 32 + qcol;
+    asm volatile("" : "+v"(i));
+    uint64_t any = 0;
+#pragma unroll
+    for (int k = 0; k < kMaskWords; ++k) any |= anc_lds[i * kMaskWords + k];
+    return any != 0;
   };
 
   // Per-lane LDS address pieces.
@@ -462,11 +516,11 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // tail or the end of the sequence need this; register i holds key
   // k0 + (i/4)*8 + 4*half + i%4).
   auto mask_tile = [&](f32x16_t& sacc, int k0) {
-    const uint64_t anc = row_anc();
+    const uint32_t hwin = row_window(k0 - w.P) >> (4 * half);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
-      const bool tail_bit = ((anc >> ((j - w.P) & 63)) & 1ull) != 0;
+      const bool tail_bit = ((hwin >> ((i >> 2) * 8 + (i & 3))) & 1u) != 0;
       const bool vis = (j < w.P) | ((j < w.N) & tail_bit);
       sacc[i] = vis ? sacc[i] : -INFINITY;
     }
@@ -531,7 +585,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // 32*(4*wave + f4) + (i/4)*8 + 4*half + i%4 of row 32*rb + qcol.
   //
   // The partial arrays have a.part_rows (a multiple of kRows) rows per split,
-  // so the rows past rows_per_seq of the last row block have room and every
+  // so the rows past T_b * H of the last row block have room and every
   // store below is unconditional: exactly kPartialStores vector-memory
   // instructions, which the wait after a split boundary relies on.
   auto emit_partial = [&](int c, float l_part) {
@@ -541,7 +595,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     asm volatile("" : "+v"(lq));
     const int qcol = lq & 31, half = lq >> 5;
     const float l_tot = l_part + swap_halves(l_part);
-    const bool node_ok = row_anc() != 0;
+    const bool node_ok = row_valid();
     mfma_result_wait();  // the last PV MFMAs may have just been issued
     // (m, l) of the row; both lanes of a row hold the same values.
     const int64_t prow = (int64_t)c * a.part_rows + w.rb * kRows + wave * 32 + qcol;
@@ -581,7 +635,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   auto emit_final = [&]() {
     const float l_tot = l_run + swap_halves(l_run);
     float2* stats = (float2*)pbuf0;  // the P buffers are free after the loop
-    const bool node_ok = row_anc() != 0;
+    const bool node_ok = row_valid();
     mfma_result_wait();
     __syncthreads();
     if (half == 0) stats[wave * 32 + qcol] = make_float2(node_ok ? m_ref : NAN, l_tot);
@@ -589,10 +643,10 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int r = w.rb * kRows + rb * 32 + qcol;
-      if (r >= a.rows_per_seq) continue;
+      if (r >= w.rows) continue;
       const float2 st = stats[rb * 32 + qcol];
       const bool ok = !(st.x != st.x);
-      const int64_t g = (int64_t)w.b * a.rows_per_seq + r;
+      const int64_t g = (int64_t)w.node0 * H + r;
       float* dst = a.out + g * kDl;
       const float mul = ok ? 1.f / st.y : NAN;
       if (wave == 0 && half == 0 && a.lse) a.lse[g] = ok ? (st.x + __log2f(st.y)) * kLn2 : NAN;
@@ -806,6 +860,8 @@ constexpr int kRows = 32;
 constexpr int kRowBytes = kDk * 4 + 16;                 // kv_c | k_pe, padded
 constexpr int kTileBytes = kKeysPerTile * kRowBytes;
 constexpr int kSmem = kTileBytes + kRows * kRowBytes;   // tile + Q rows
+// Trees above 64 nodes build their masks in the tile buffer before the first tile.
+static_assert(kTreeScratchBytes <= kTileBytes, "tree mask scratch");
 }  // namespace f32k
 
 __global__ void __launch_bounds__(f32k::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -815,24 +871,38 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
   char* const qs = smem + kTileBytes;
 
   BlockWork w;
-  if (!map_block(a, w)) return;
-  const int T = a.tree_nodes, H = a.heads;
+  if (!map_block(a, w, kRows)) return;
+  const int H = a.heads;
   const int lane = lane_id();
   const int half = lane >> 5;
   const int qcol = lane & 31;
   const int r_local = w.rb * kRows + qcol;
-  const bool row_ok = r_local < a.rows_per_seq;
-  const int r_eff = row_ok ? r_local : a.rows_per_seq - 1;
-  const int64_t grow = (int64_t)w.b * a.rows_per_seq + r_eff;
-  const uint64_t tmask = wave_tree_mask(a.parents + (int64_t)w.b * T, T);
-  const uint64_t anc = node_mask(tmask, r_eff / H);
-  const bool node_ok = w.seq_ok && anc != 0;
+  const bool row_ok = r_local < w.rows;
+  const int r_eff = row_ok ? r_local : w.rows - 1;
+  const int64_t grow = (int64_t)w.node0 * H + r_eff;
+  // Ancestor mask words of this lane's row: the one-wave builder for trees of
+  // up to 64 nodes, else the workgroup builder in the (not yet used) tile buffer.
+  uint64_t anc[kMaskWords];
+  if (w.T <= 64) {
+    anc[0] = node_mask(wave_tree_mask(a.parents + w.node0, w.T), r_eff / H);
+#pragma unroll
+    for (int k = 1; k < kMaskWords; ++k) anc[k] = 0ull;
+  } else {
+    block_tree_masks<kThreads>(a.parents + w.node0, w.T, smem);
+    const uint64_t* src = tree_scratch_masks(smem) + (r_eff / H) * kMaskWords;
+#pragma unroll
+    for (int k = 0; k < kMaskWords; ++k) anc[k] = src[k];
+  }
+  uint64_t any = 0;
+#pragma unroll
+  for (int k = 0; k < kMaskWords; ++k) any |= anc[k];
+  const bool node_ok = w.seq_ok && any != 0;
 
   // Q rows of the block into LDS: row qr = [q_nope | q_pe].
   for (int idx = lane; idx < kRows * 144; idx += 64) {
     const int qr = idx / 144, ch = idx % 144;
-    const int rr = min(w.rb * kRows + qr, a.rows_per_seq - 1);
-    const int64_t gr = (int64_t)w.b * a.rows_per_seq + rr;
+    const int rr = min(w.rb * kRows + qr, w.rows - 1);
+    const int64_t gr = (int64_t)w.node0 * H + rr;
     const float* src = ch < 128 ? (const float*)a.q_nope + gr * kDl + ch * 4
                                 : (const float*)a.q_pe + gr * kDr + (ch - 128) * 4;
     *(u32x4_t*)(qs + qr * kRowBytes + ch * 16) = *(const u32x4_t*)src;
@@ -891,7 +961,15 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k_rd[2 * kc], q_rd[2 * kc], sacc, 0, 0, 0);
 
       float sv[16];
-      const float mx = mask_scale_max(sv, sacc, a.scale_log2, k0, half, w.P, w.N, anc);
+      const int u0 = k0 - w.P, w0 = min(max(u0, 0) >> 6, kMaskWords - 1);
+      uint64_t lo = anc[0], hi = anc[1];
+#pragma unroll
+      for (int k = 1; k < kMaskWords; ++k) {
+        lo = w0 == k ? anc[k] : lo;
+        hi = w0 + 1 == k ? anc[k] : hi;
+      }
+      if (w0 + 1 >= kMaskWords) hi = 0ull;
+      const float mx = mask_scale_max(sv, sacc, a.scale_log2, k0, half, w.P, w.N, mask_window(u0, lo, hi));
       m_max = fmaxf(m_max, mx);
       if (m_ref == -INFINITY) m_ref = mx;
       overflow |= mx > m_ref + kOverflowSlack;
@@ -972,16 +1050,19 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   __shared__ float wsh[kCombineRows][kCombineStage];
   __shared__ float lsh[kCombineRows][kCombineGroups];
   __shared__ f32x4_t accsh[kCombineRows][kCombineGroups - 1][32][4];
-  const int row_groups = (a.rows_per_seq + kCombineRows - 1) / kCombineRows;
+  const int row_groups = (a.max_rows_per_seq + kCombineRows - 1) / kCombineRows;
   const int b = (int)(blockIdx.x / row_groups);
+  const int node0 = a.node_offset[b];
+  const int rows = (a.node_offset[b + 1] - node0) * a.heads;
   const int tid = threadIdx.x;
   const int j = tid / (32 * kCombineGroups), grp = (tid >> 5) % kCombineGroups, t32 = tid & 31;
   const int r = (int)(blockIdx.x % row_groups) * kCombineRows + j;
   const int s0 = a.split_offset[b];
   const int S = a.split_offset[b + 1] - s0;
-  if (S <= 1) return;
-  const bool live = r < a.rows_per_seq;
-  const int rr = live ? r : a.rows_per_seq - 1;
+  // Whole workgroup: no split partials, or every row past this sequence's rows.
+  if (S <= 1 || (int)(blockIdx.x % row_groups) * kCombineRows >= rows) return;
+  const bool live = r < rows;
+  const int rr = live ? r : rows - 1;
   const float* ml = a.part_ml + 2 * ((int64_t)s0 * a.part_rows + rr);
   const int64_t ml_stride = 2 * (int64_t)a.part_rows;
 
@@ -1053,7 +1134,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   for (int g = 0; g < kCombineGroups - 1; ++g)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] += accsh[j][g][t32][q];
-  const int64_t grow = (int64_t)b * a.rows_per_seq + r;
+  const int64_t grow = (int64_t)node0 * a.heads + r;
   const float inv = nan ? NAN : 1.f / lloc;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1069,6 +1150,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
 // ===========================================================================
 int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (grid_blocks == 0) return 0;  // no tree nodes in the batch
   if (dtype == MLA_DTYPE_BF16)
     hipLaunchKernelGGL(mla_verify_attn_bf16_kernel, dim3((unsigned)grid_blocks), dim3(bf16k::kThreads), 0,
                        st, a);
@@ -1079,7 +1161,8 @@ int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks,
 }
 
 int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream) {
-  const int64_t groups = (int64_t)a.batch * ((a.rows_per_seq + kCombineRows - 1) / kCombineRows);
+  const int64_t groups = (int64_t)a.batch * ((a.max_rows_per_seq + kCombineRows - 1) / kCombineRows);
+  if (groups == 0) return 0;
   if (dtype == MLA_DTYPE_BF16)
     hipLaunchKernelGGL(mla_verify_combine_kernel<__bf16>, dim3((unsigned)groups), dim3(kCombineThreads), 0,
                        (hipStream_t)stream, a);
@@ -1091,8 +1174,8 @@ int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream) {
 
 int launch_tree_masks(const int32_t* parents, int32_t batch, int32_t tree_nodes, uint64_t* masks,
                       void* stream) {
-  hipLaunchKernelGGL(mla_tree_masks_kernel, dim3(batch), dim3(64), 0, (hipStream_t)stream, parents,
-                     tree_nodes, masks);
+  hipLaunchKernelGGL(mla_tree_masks_kernel, dim3(batch), dim3(kTreeMaskThreads), 0, (hipStream_t)stream,
+                     parents, tree_nodes, masks);
   return (int)hipGetLastError();
 }
 

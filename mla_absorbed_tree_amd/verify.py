@@ -16,32 +16,36 @@ class MlaVerify:
 
     kv_lens are the host copies of N_b (prefix + tree nodes per sequence) that
     size the split schedule; the device kv_indptr passed at call time may
-    describe other lengths (each still >= tree_nodes).
+    describe other lengths (each still >= the sequence's tree size).
+    tree_lens gives every sequence its own tree size (packed trees, each in
+    0..tree_nodes); None means tree_nodes nodes everywhere.
     """
 
     def __init__(self, batch: int, heads: int, tree_nodes: int, dtype: str,
                  kv_lens: Sequence[int], num_splits: int = 0, kv_c_row_stride: int = 512,
-                 k_pe_row_stride: int = 64, device="cuda"):
+                 k_pe_row_stride: int = 64, device="cuda",
+                 tree_lens: Optional[Sequence[int]] = None):
         self.dtype_code, self.torch_dtype = _DTYPES[dtype]
         self.batch, self.heads, self.tree_nodes = batch, heads, tree_nodes
+        self.nodes = batch * tree_nodes if tree_lens is None else int(np.sum(tree_lens))
         self.plan = None
         self.plan, self.workspace_bytes = B.mla_verify_plan(
             batch, heads, tree_nodes, self.dtype_code, kv_lens, num_splits,
-            kv_c_row_stride, k_pe_row_stride)
+            kv_c_row_stride, k_pe_row_stride, tree_len_host=tree_lens)
         self.info = B.mla_verify_plan_get_info(self.plan)
         self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=device)
 
     def __call__(self, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents, scale,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                  stream=None):
-        rows = self.batch * self.tree_nodes
+        rows = self.nodes
         for name, t in (("q_nope", q_nope), ("q_pe", q_pe), ("kv_c", kv_c), ("k_pe", k_pe)):
             if t.dtype != self.torch_dtype or not t.is_cuda:
                 raise TypeError("%s must be a %s device tensor" % (name, self.torch_dtype))
         if tuple(q_nope.shape) != (rows, self.heads, 512) or not q_nope.is_contiguous():
-            raise ValueError("q_nope must be contiguous [batch*T, H, 512]")
+            raise ValueError("q_nope must be contiguous [nodes, H, 512]")
         if tuple(q_pe.shape) != (rows, self.heads, 64) or not q_pe.is_contiguous():
-            raise ValueError("q_pe must be contiguous [batch*T, H, 64]")
+            raise ValueError("q_pe must be contiguous [nodes, H, 64]")
         for name, t in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("tree_parents", tree_parents)):
             if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
                 raise TypeError("%s must be a contiguous int32 device tensor" % name)

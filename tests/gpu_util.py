@@ -26,8 +26,9 @@ def run_hip(x, num_splits=0, kv_c=None, k_pe=None, strides=None, device_tensors=
     d = device_tensors or device_inputs(x)
     cfg = x.cfg
     kc_stride, kp_stride = strides or (512, 64)
+    ragged = x.parents.ndim == 1
     mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, num_splits,
-                   kc_stride, kp_stride)
+                   kc_stride, kp_stride, tree_lens=x.tree_lens if ragged else None)
     o, lse = mv(d["q_nope"], d["q_pe"], d["kv_c"] if kv_c is None else kv_c,
                 d["k_pe"] if k_pe is None else k_pe, d["kv_indptr"], d["kv_indices"],
                 d["tree_parents"], x.scale)
@@ -39,7 +40,7 @@ def run_hip(x, num_splits=0, kv_c=None, k_pe=None, strides=None, device_tensors=
 
 def run_oracle(x, nodes=None):
     return verify_attention(x.q_nope, x.q_pe, x.kv_c, x.k_pe, x.kv_indptr, x.kv_indices,
-                            x.parents, x.scale, nodes=nodes)
+                            x.parents, x.scale, nodes=nodes, tree_indptr=x.tree_indptr)
 
 
 def compare(o, lse, o_ref, lse_ref, dtype, what=""):
@@ -64,6 +65,5 @@ def compare(o, lse, o_ref, lse_ref, dtype, what=""):
 
 
 def node_rows(x, nodes):
-    """Row indices (b*T + t) of the given (b, t) nodes."""
-    T = x.cfg.tree_nodes
-    return np.array([b * T + t for b, t in nodes])
+    """Packed row indices (tree_indptr[b] + t) of the given (b, t) nodes."""
+    return np.array([int(x.tree_indptr[b]) + t for b, t in nodes])

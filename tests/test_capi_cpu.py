@@ -47,10 +47,11 @@ def test_status_strings(B):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), -1), (dict(batch=257), -1), (dict(num_heads=0), -1),
-    (dict(tree_nodes=0), -1), (dict(tree_nodes=65), -2), (dict(d_latent=256), -2),
+    (dict(tree_nodes=0), -1), (dict(tree_nodes=257), -2), (dict(d_latent=256), -2),
     (dict(d_rope=32), -2), (dict(dtype=7), -1), (dict(kv_c_row_stride=500), -1),
     (dict(kv_c_row_stride=516), -1), (dict(k_pe_row_stride=60), -1), (dict(num_splits=-1), -1),
-    (dict(kv_len_host=[10, 3]), -1)])
+    (dict(kv_len_host=[10, 3]), -1), (dict(tree_len_host=[3, 9]), -1),
+    (dict(tree_len_host=[-1, 2]), -1), (dict(tree_len_host=[8, 8], kv_len_host=[100, 7]), -1)])
 def test_plan_rejects_bad_problems(B, kw, status):
     args = dict(batch=2, num_heads=4, tree_nodes=8, dtype=1, kv_len_host=[100, 50])
     args.update(kw)
@@ -130,6 +131,32 @@ def test_run_argument_checks_happen_before_any_launch(B):
             B.mla_verify_run(p, *args, bad, fake, fake, fake, ws, stream=0)
         assert e.value.status == B.MLA_ERR_INVALID_ARG
     with pytest.raises(B.MlaVerifyError) as e:
-        B.mla_verify_tree_masks(fake, 1, 65, fake, stream=0)
+        B.mla_verify_tree_masks(fake, 1, 257, fake, stream=0)
     assert e.value.status == B.MLA_ERR_INVALID_ARG
     B.mla_verify_plan_destroy(p)
+
+
+def test_ragged_tree_plans(B):
+    # Row blocks are counted for the largest tree (200 nodes x 8 heads = 13
+    # blocks of 128 rows); the sequence without nodes gets no split, and
+    # splits are sized by the work each sequence really has.
+    p, ws = B.mla_verify_plan(3, 8, 256, 1, [5000, 300, 9000], tree_len_host=[200, 0, 1])
+    info = B.mla_verify_plan_get_info(p)
+    assert info["rows_per_block"] == 128
+    assert info["grid_blocks"] % 13 == 0
+    # 13 * 157 + 1 * 282 = 2323 tiles of work over 256 CUs -> chunks of 10
+    # tiles; 157 tiles -> 16 splits, 282 tiles -> 29 splits, none for the empty tree.
+    assert info["total_splits"] == 16 + 29 and info["uses_combine"] == 1
+    B.mla_verify_plan_destroy(p)
+    # every tree empty: a valid plan with nothing to launch
+    p, ws = B.mla_verify_plan(2, 64, 16, 1, [100, 100], tree_len_host=[0, 0])
+    info = B.mla_verify_plan_get_info(p)
+    assert info["grid_blocks"] == 0 and info["total_splits"] == 0 and info["uses_combine"] == 0
+    B.mla_verify_plan_destroy(p)
+    # equal tree sizes given explicitly plan exactly like tree_len_host = NULL
+    for kw in (dict(), dict(num_splits=256)):
+        a, wa = B.mla_verify_plan(4, 64, 64, 1, [32832] * 4, **kw)
+        b, wb = B.mla_verify_plan(4, 64, 64, 1, [32832] * 4, tree_len_host=[64] * 4, **kw)
+        assert B.mla_verify_plan_get_info(a) == B.mla_verify_plan_get_info(b) and wa == wb
+        B.mla_verify_plan_destroy(a)
+        B.mla_verify_plan_destroy(b)

@@ -9,6 +9,8 @@ of synthetic inputs that already sit in HBM. The primary workload is the
 compaction of the paged workload's 600k-slot pool (its kernel's HBM rate, and
 the verify step on the scattered against the compacted pool) in "kv_compact",
 and the token-acceptance launch that follows a verify step in "tree_accept".
+A batch of packed trees of 1..256 nodes per sequence (32k prefix) is reported in
+"also" as well.
 
 Prints ONE JSON line. `value` is KV tokens/s (sum of N_b per step / step time);
 `roofline` describes the attention kernel (algorithmic FLOPs per launch over
@@ -33,6 +35,7 @@ PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
 PRIMARY = "b4_h64_p32768_t64_bf16"
 ALSO = "b1_h64_p200000_t32_bf16_s256"
+RAGGED = "b4_h64_p32768_t1to256_ragged_bf16"
 
 
 def log(msg):
@@ -54,17 +57,21 @@ def algorithmic_counts(x):
     sequence b sees P_b prefix keys plus its ancestors-or-self.
     Bytes = KV (576 elements per token) + page-table entries + Q + out/lse +
     parents; split partials are not algorithmic and are counted apart.
+    Trees may differ in size per sequence (packed, x.tree_indptr).
     """
     cfg = x.cfg
     e = 2 if cfg.dtype == "bf16" else 4
-    H, T = cfg.heads, cfg.tree_nodes
+    H = cfg.heads
+    flat = x.parents.reshape(-1)
     pairs = 0
     for b in range(cfg.batch):
-        pairs += T * int(x.prefix_lens[b]) + int(tree_depths(x.parents[b]).sum())
+        par = flat[x.tree_indptr[b]:x.tree_indptr[b + 1]]
+        pairs += len(par) * int(x.prefix_lens[b]) + int(tree_depths(par).sum())
     flops = 2.0 * H * (576 + 512) * pairs
     kv_tokens = int(x.kv_lens.sum())
-    rows = cfg.batch * T * H
-    bytes_ = kv_tokens * 576 * e + kv_tokens * 4 + rows * 576 * e + rows * 513 * 4 + cfg.batch * T * 4
+    nodes = int(x.tree_indptr[-1])
+    rows = nodes * H
+    bytes_ = kv_tokens * 576 * e + kv_tokens * 4 + rows * 576 * e + rows * 513 * 4 + nodes * 4
     return flops, bytes_, kv_tokens, pairs
 
 
@@ -80,8 +87,10 @@ def bench_workload(name, steps, warmup, num_splits=None):
     flops, bytes_, kv_tokens, pairs = algorithmic_counts(x)
     d = device_inputs(x)
     splits = cfg.num_splits if num_splits is None else num_splits
-    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, splits)
-    rows = cfg.batch * cfg.tree_nodes
+    ragged = x.parents.ndim == 1
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, splits,
+                   tree_lens=x.tree_lens if ragged else None)
+    rows = int(x.tree_indptr[-1])
     out = torch.empty((rows, cfg.heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((rows, cfg.heads), dtype=torch.float32, device="cuda")
     args = (d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"], d["kv_indices"],
@@ -130,7 +139,8 @@ def bench_workload(name, steps, warmup, num_splits=None):
                      "flops_per_launch": flops, "avg_launch_ms": attn_ms},
         "config": {"workload": name, "batch": cfg.batch, "heads": cfg.heads,
                    "prefix": cfg.prefix if cfg.prefix is not None else list(cfg.prefix_range),
-                   "tree_nodes": cfg.tree_nodes, "kv_layout": cfg.layout,
+                   "tree_nodes": cfg.tree_nodes if not ragged else [int(t) for t in x.tree_lens],
+                   "kv_layout": cfg.layout,
                    "num_splits": mv.info["total_splits"] // cfg.batch if cfg.batch == 1 else "auto",
                    "d_latent": 512, "d_rope": 64, "kv_dtype": cfg.dtype, "out_dtype": "f32"},
     }
@@ -312,10 +322,11 @@ def main():
 
     res, x = bench_workload(a.workload, a.steps, a.warmup, a.num_splits)
     also = []
-    if not a.no_also and a.workload != ALSO:
-        r2, _ = bench_workload(ALSO, a.steps, a.warmup)
-        also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "hbm_gbps", "hbm_frac",
-                                        "mfma_frac", "kernels_ms", "roofline", "config", "plan")})
+    if not a.no_also and a.workload == PRIMARY:
+        for name in (ALSO, RAGGED):
+            r2, _ = bench_workload(name, a.steps, a.warmup)
+            also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "hbm_gbps", "hbm_frac",
+                                            "mfma_frac", "kernels_ms", "roofline", "config", "plan")})
     compact = accept = None
     if not a.no_also and not a.no_compact:
         compact = bench_kv_compact(a.steps, a.warmup)

@@ -70,8 +70,18 @@ CONFIGS = {
 # Order used by tests and docs: small parity case first, then the four large ones.
 CONFIG_ORDER = list(CONFIGS)
 
+# Further measured workloads (not among the five above): packed trees of 1..256
+# nodes per sequence at the 32k prefix, random parents.
+EXTRA_WORKLOADS = {
+    c.name: c
+    for c in (
+        VerifyConfig(name="b4_h64_p32768_t1to256_ragged_bf16", batch=4, heads=64, tree_nodes=256,
+                     tree_range=(1, 256), dtype="bf16", prefix=32768, seed=5),
+    )
+}
+
 
 def get_config(name: str, **overrides) -> VerifyConfig:
     """Return the named workload, optionally with fields replaced (for tests)."""
-    cfg = CONFIGS[name]
+    cfg = CONFIGS[name] if name in CONFIGS else EXTRA_WORKLOADS[name]
     return dataclasses.replace(cfg, **overrides) if overrides else cfg

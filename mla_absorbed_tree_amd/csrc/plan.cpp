@@ -16,6 +16,71 @@ std::string fmt(const char* f, long long a = 0, long long b = 0) {
   return buf;
 }
 
+// Launch-time model of the attention kernel, in units of one workgroup's key
+// tile. Split groups are dealt round-robin to the XCDs, all row blocks of a
+// group on one XCD and in order (as map_block does); each XCD runs one
+// workgroup per compute unit at a time and hands the next one, in dispatch
+// order, to the first unit that frees up. A workgroup costs its split's tiles
+// plus a fixed start-up (Q and tree loads, pipeline fill, epilogue). Split
+// partials add their write and the combine's read at HBM speed.
+constexpr double kWgOverheadTiles = 4.0;
+constexpr double kTileSeconds = 1.85e-6;      // one tile of one 128-row workgroup (measured)
+constexpr double kHbmBytesPerSecond = 5.0e12; // sustained partial write/read rate
+
+double estimate_launch(const std::vector<int64_t>& tiles, const std::vector<int64_t>& row_blocks,
+                       const std::vector<int32_t>& splits, int rows_per_block, int dtype) {
+  const int cus_per_xcd = kComputeUnits / kXcds;
+  std::vector<std::vector<double>> free_at(kXcds, std::vector<double>(cus_per_xcd, 0.0));
+  int64_t cg = 0;
+  double partial_bytes = 0.0;
+  const double part_row_bytes = dtype == MLA_DTYPE_BF16 ? kDl * 2 + 8 : kDl * 4 + 8;
+  for (size_t b = 0; b < tiles.size(); ++b) {
+    const int64_t S = splits[b];
+    if (S > 1) partial_bytes += double(S) * double(row_blocks[b]) * rows_per_block * part_row_bytes;
+    for (int64_t s = 0; s < S; ++s, ++cg) {
+      const int64_t nt = (s + 1) * tiles[b] / S - s * tiles[b] / S;
+      std::vector<double>& cu = free_at[cg % kXcds];
+      for (int64_t rb = 0; rb < row_blocks[b]; ++rb) {
+        auto it = std::min_element(cu.begin(), cu.end());
+        *it += double(nt) + kWgOverheadTiles;
+      }
+    }
+  }
+  double makespan = 0.0;
+  for (const auto& cu : free_at) makespan = std::max(makespan, *std::max_element(cu.begin(), cu.end()));
+  return makespan * kTileSeconds + 2.0 * partial_bytes / kHbmBytesPerSecond;
+}
+
+// Automatic split counts: candidate chunk lengths ceil(max_tiles / k),
+// k = 1, 2, ..., no shorter than kMinChunkTiles (a split's partial costs
+// about a few tiles); S_b = ceil(tiles_b / chunk). The estimate decides; a
+// candidate must beat the best so far by 1% (ties keep fewer splits).
+std::vector<int32_t> choose_auto_splits(const std::vector<int64_t>& tiles,
+                                        const std::vector<int64_t>& row_blocks, int rows_per_block, int dtype) {
+  constexpr int64_t kMinChunkTiles = 8;
+  constexpr int64_t kMaxCandidates = 512;
+  const int64_t max_tiles = tiles.empty() ? 0 : *std::max_element(tiles.begin(), tiles.end());
+  std::vector<int32_t> best(tiles.size(), 0), cand(tiles.size(), 0);
+  double best_t = -1.0;
+  int64_t last_chunk = -1;
+  for (int64_t k = 1; k <= kMaxCandidates; ++k) {
+    const int64_t chunk = std::max<int64_t>(kMinChunkTiles, (max_tiles + k - 1) / k);
+    if (chunk == last_chunk) {
+      if (chunk == kMinChunkTiles) break;
+      continue;
+    }
+    last_chunk = chunk;
+    for (size_t b = 0; b < tiles.size(); ++b)
+      cand[b] = tiles[b] > 0 ? int32_t(std::max<int64_t>(1, (tiles[b] + chunk - 1) / chunk)) : 0;
+    const double t = estimate_launch(tiles, row_blocks, cand, rows_per_block, dtype);
+    if (best_t < 0.0 || t < 0.99 * best_t) {
+      best_t = t;
+      best = cand;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err) {
@@ -94,7 +159,6 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   // without tree nodes has none and gets no split).
   plan.kv_len.resize(p.batch);
   std::vector<int64_t> tiles(p.batch), row_blocks(p.batch);
-  int64_t work = 0, busy_row_blocks = 0;
   for (int b = 0; b < p.batch; ++b) {
     const int32_t n = p.kv_len_host[b];
     if (n < tree_len[b]) {
@@ -104,42 +168,17 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
     plan.kv_len[b] = n;
     row_blocks[b] = (int64_t(tree_len[b]) * p.num_heads + plan.rows_per_block - 1) / plan.rows_per_block;
     tiles[b] = row_blocks[b] > 0 ? (int64_t(n) + kKeysPerTile - 1) / kKeysPerTile : 0;
-    work += row_blocks[b] * tiles[b];
-    busy_row_blocks += tiles[b] > 0 ? row_blocks[b] : 0;
   }
 
-  // Split schedule. Forced: S_b = min(num_splits, tiles_b). Automatic: pick a
-  // chunk length (in tiles) so that the launch holds about one workgroup per
-  // compute unit, but never chunks shorter than kMinChunkTiles (a split's
-  // partial write costs about as much as a few tiles of compute).
-  constexpr int64_t kMinChunkTiles = 8;
+  // Split schedule. Forced: S_b = min(num_splits, tiles_b). Automatic: the
+  // chunk length (in tiles, at least kMinChunkTiles) whose estimated launch
+  // time is smallest (choose_auto_splits).
   plan.splits.resize(p.batch);
   if (p.num_splits > 0) {
     for (int b = 0; b < p.batch; ++b)
       plan.splits[b] = int32_t(std::min<int64_t>(p.num_splits, tiles[b]));
   } else {
-    if (busy_row_blocks >= kComputeUnits) {
-      for (int b = 0; b < p.batch; ++b) plan.splits[b] = tiles[b] > 0 ? 1 : 0;
-    } else {
-      const int64_t chunk = std::max<int64_t>(kMinChunkTiles, (work + kComputeUnits - 1) / kComputeUnits);
-      for (int b = 0; b < p.batch; ++b)
-        plan.splits[b] = tiles[b] > 0 ? int32_t(std::max<int64_t>(1, (tiles[b] + chunk - 1) / chunk)) : 0;
-    }
-    // Every KV chunk runs on one XCD (its row blocks share that XCD's L2):
-    // with fewer chunks than XCDs some XCDs would idle, so split the longest
-    // sequences further (while chunks stay at least kMinChunkTiles long).
-    for (;;) {
-      int64_t total = 0;
-      for (int b = 0; b < p.batch; ++b) total += plan.splits[b];
-      if (total >= kXcds) break;
-      int best = -1;
-      for (int b = 0; b < p.batch; ++b) {
-        if (tiles[b] == 0 || tiles[b] / (plan.splits[b] + 1) < kMinChunkTiles) continue;
-        if (best < 0 || tiles[b] * plan.splits[best] > tiles[best] * plan.splits[b]) best = b;
-      }
-      if (best < 0) break;
-      ++plan.splits[best];
-    }
+    plan.splits = choose_auto_splits(tiles, row_blocks, plan.rows_per_block, p.dtype);
   }
   plan.split_offset.assign(p.batch + 1, 0);
   for (int b = 0; b < p.batch; ++b) {
@@ -151,9 +190,10 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   // Many short splits (a forced split count) would make thousands of
   // workgroups that each pay the fixed start-up and tail; instead one
   // workgroup runs several consecutive splits, aiming at about one workgroup
-  // per compute unit. The bf16 kernel only (the fp32 kernel runs one split).
+  // per compute unit. The bf16 kernel only (the fp32 kernel runs one split);
+  // automatic splits are already sized for the chip (one split each).
   plan.group = 1;
-  if (p.dtype == MLA_DTYPE_BF16) {
+  if (p.dtype == MLA_DTYPE_BF16 && p.num_splits > 0) {
     int64_t split_row_blocks = 0;
     for (int b = 0; b < p.batch; ++b) split_row_blocks += int64_t(plan.splits[b]) * row_blocks[b];
     plan.group = int32_t(std::max<int64_t>(1, split_row_blocks / kComputeUnits));

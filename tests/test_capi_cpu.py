@@ -144,8 +144,8 @@ def test_ragged_tree_plans(B):
     info = B.mla_verify_plan_get_info(p)
     assert info["rows_per_block"] == 128
     assert info["grid_blocks"] % 13 == 0
-    # 13 * 157 + 1 * 282 = 2323 tiles of work over 256 CUs -> chunks of 10
-    # tiles; 157 tiles -> 16 splits, 282 tiles -> 29 splits, none for the empty tree.
+    # 157 and 282 tiles, one chunk length for both (10 tiles: 16 and 29
+    # splits), none for the empty tree.
     assert info["total_splits"] == 16 + 29 and info["uses_combine"] == 1
     B.mla_verify_plan_destroy(p)
     # every tree empty: a valid plan with nothing to launch

@@ -260,7 +260,7 @@ def measured_traffic(workload):
     if prof.get("kernel_code_sha256") != sha:
         return None
     w = prof.get("workloads", {}).get(workload)
-    return None if w is None else float(w["traffic_bytes"])
+    return None if w is None or "traffic_bytes" not in w else float(w["traffic_bytes"])
 
 
 def cpu_baseline(x, budget_s=15.0):

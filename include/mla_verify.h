@@ -70,9 +70,11 @@ typedef struct {
   const int32_t* tree_len_host; /* host [batch]: T_b, the tree nodes of sequence b, each in
                                    0..tree_nodes (0: the sequence has no query this step),
                                    or NULL: every sequence has tree_nodes nodes. Read during
-                                   the call only; fixed for the plan's runs. The pages ask for
-                                   trees of arbitrary size ["Ground Truth in Silicon" page,
-                                   "Input Knowledge Required", item 3]. */
+                                   the call only; fixed for the plan's runs. The pages give
+                                   the verify kernel a set of query nodes, the tree's
+                                   leaves and internal nodes, with no bound on their
+                                   number ["Ground Truth in Silicon" page, "Input
+                                   Knowledge Required", item 3]. */
 } mla_verify_problem;
 
 #define MLA_VERIFY_MAX_BATCH 256

@@ -1,6 +1,7 @@
 """Pins of the oracle's packed ("ragged") trees and of trees above 64 nodes.
 
-The pages ask for draft trees of arbitrary size ("Ground Truth in Silicon"
+The pages give the verify kernel a set of query nodes (the draft tree's leaves
+and internal nodes) with no bound on their number ("Ground Truth in Silicon"
 page, "Input Knowledge Required", item 3). Each test ties the oracle to
 something other than itself: separate single-sequence runs on hand-sliced
 inputs, the scalar brute force (its own visibility walk), torch SDPA in float64

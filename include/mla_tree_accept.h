@@ -36,8 +36,8 @@
 extern "C" {
 #endif
 
-/* Largest tree the acceptance kernel handles (one node per lane of a wave). */
-#define MLA_TREE_ACCEPT_MAX_TREE 64
+/* Largest tree the acceptance kernels handle (the verify limit). */
+#define MLA_TREE_ACCEPT_MAX_TREE MLA_VERIFY_MAX_TREE
 
 /*
  *   tree_parents  device int32 [batch, T], as for mla_verify_run
@@ -49,7 +49,8 @@ extern "C" {
  *   accept_len    device int32 [batch], written
  *   accept_path   device int32 [batch, T], written
  *   bonus_token   device int32 [batch], written
- * One wave per sequence; asynchronous, allocates nothing (graph-capturable).
+ * One wave per sequence for T <= 64, one 256-lane workgroup per sequence
+ * above; asynchronous, allocates nothing (graph-capturable).
  * Errors: MLA_ERR_INVALID_ARG (NULL pointer, bad sizes; nothing launched),
  * MLA_ERR_HIP if the launch fails.
  */

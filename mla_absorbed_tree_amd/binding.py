@@ -24,7 +24,7 @@ MLA_DTYPE_F32 = 0
 MLA_DTYPE_BF16 = 1
 MLA_VERIFY_MAX_BATCH = 256
 MLA_VERIFY_MAX_TREE = 256
-MLA_TREE_ACCEPT_MAX_TREE = 64
+MLA_TREE_ACCEPT_MAX_TREE = 256
 
 # Symbols declared in include/*.h.
 EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",

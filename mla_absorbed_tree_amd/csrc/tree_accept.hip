@@ -1,5 +1,6 @@
 // Greedy token acceptance over a verified draft tree: one 64-lane wave per
-// sequence, one tree node per lane. Acceptance of a node is the AND of a local
+// sequence with one tree node per lane for trees of up to 64 nodes, one
+// 256-lane workgroup above that. Acceptance of a node is the AND of a local
 // test (its draft token equals the target's token after its parent) over its
 // ancestor-or-self set, which the shared pointer-doubling mask gives directly:
 // accepted(t) = (anc(t) & ~ok) == 0.
@@ -60,11 +61,85 @@ __global__ void __launch_bounds__(64) mla_tree_accept_kernel(const int32_t* __re
   }
 }
 
+// Trees of 65..256 nodes: thread t owns node t. The masks come from the
+// workgroup builder (kMaskWords words per node, zero on an invalid chain);
+// each wave's ballot of the local test is one word of the OK mask. The
+// deepest accepted node wins (smallest index among equals), and every slot of
+// the path row is written exactly once, from the path gathered in LDS.
+constexpr int kAcceptThreads = kMaxTreeNodes;
+__global__ void __launch_bounds__(kAcceptThreads) mla_tree_accept_large_kernel(
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ draft, const int32_t* __restrict__ target,
+    const int32_t* __restrict__ root_target, int T, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ accept_path, int32_t* __restrict__ bonus) {
+  __shared__ __attribute__((aligned(16))) char scratch[kTreeScratchBytes];
+  __shared__ uint64_t ok_words[kMaskWords];
+  __shared__ int wave_key[kAcceptThreads / 64];
+  __shared__ int path_lds[kMaxTreeNodes];
+  const int b = blockIdx.x;
+  const int t = threadIdx.x, wave = t >> 6;
+  const bool live = t < T;
+  const int64_t base = (int64_t)b * T;
+  block_tree_masks<kAcceptThreads>(parents + base, T, scratch);
+  const uint64_t* anc = tree_scratch_masks(scratch) + t * kMaskWords;
+  uint64_t any = 0;
+  int depth = 0;
+  if (live) {
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) {
+      any |= anc[w];
+      depth += __popcll(anc[w]);
+    }
+  }
+  const int root_tok = root_target[b];
+  bool ok = false;
+  if (live && any != 0) {
+    const int par = parents[base + t];
+    const int want = par < 0 ? root_tok : target[base + par];
+    ok = draft[base + t] == want;
+  }
+  const uint64_t ballot = __ballot(ok);
+  if ((t & 63) == 0) ok_words[wave] = ballot;
+  __syncthreads();
+  bool accepted = live && any != 0;
+  if (accepted) {
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) accepted &= (anc[w] & ~ok_words[w]) == 0;
+  }
+  // Deepest accepted node, smallest index among equals: maximise
+  // depth * kMaxTreeNodes + (kMaxTreeNodes - 1 - t) over the workgroup.
+  int key = accepted ? depth * kMaxTreeNodes + (kMaxTreeNodes - 1 - t) : -1;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) key = max(key, shfl_i32(key, lane_id() ^ off));
+  if ((t & 63) == 0) wave_key[wave] = key;
+  __syncthreads();
+  key = wave_key[0];
+#pragma unroll
+  for (int w = 1; w < kAcceptThreads / 64; ++w) key = max(key, wave_key[w]);
+  const int len = key < 0 ? 0 : key / kMaxTreeNodes;
+  const int best = key < 0 ? -1 : kMaxTreeNodes - 1 - key % kMaxTreeNodes;
+  // The nodes of the winner's path: node u is on it iff bit u of its mask is set.
+  if (best >= 0 && live) {
+    const uint64_t* pm = tree_scratch_masks(scratch) + best * kMaskWords;
+    if ((pm[t >> 6] >> (t & 63)) & 1ull) path_lds[depth - 1] = t;
+  }
+  __syncthreads();
+  if (live) accept_path[base + t] = t < len ? path_lds[t] : -1;
+  if (t == 0) {
+    accept_len[b] = len;
+    bonus[b] = best < 0 ? root_tok : target[base + best];
+  }
+}
+
 int launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target,
                        const int32_t* root_target, int32_t batch, int32_t T, int32_t* accept_len,
                        int32_t* accept_path, int32_t* bonus, void* stream) {
-  hipLaunchKernelGGL(mla_tree_accept_kernel, dim3((unsigned)batch), dim3(64), 0, (hipStream_t)stream, parents,
-                     draft, target, root_target, (int)T, accept_len, accept_path, bonus);
+  if (T <= 64)
+    hipLaunchKernelGGL(mla_tree_accept_kernel, dim3((unsigned)batch), dim3(64), 0, (hipStream_t)stream, parents,
+                       draft, target, root_target, (int)T, accept_len, accept_path, bonus);
+  else
+    hipLaunchKernelGGL(mla_tree_accept_large_kernel, dim3((unsigned)batch), dim3(kAcceptThreads), 0,
+                       (hipStream_t)stream, parents, draft, target, root_target, (int)T, accept_len, accept_path,
+                       bonus);
   return (int)hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ def _run(B, parents, draft, target, root):
 
 
 @pytest.mark.parametrize("kind", ["uniform", "bounded", "chain"])
-@pytest.mark.parametrize("T", [1, 2, 7, 31, 32, 33, 63, 64])
+@pytest.mark.parametrize("T", [1, 2, 7, 31, 32, 33, 63, 64, 65, 100, 128, 129, 200, 255, 256])
 def test_matches_oracle(B, kind, T):
     rng = np.random.default_rng(1000 + T + 100 * ["uniform", "bounded", "chain"].index(kind))
     Bn = 24

@@ -67,7 +67,7 @@ def _brute_force(parents, draft, target, root):
 @pytest.mark.parametrize("kind", ["uniform", "bounded", "chain"])
 def test_brute_force_agrees(kind):
     rng = np.random.default_rng({"uniform": 10, "bounded": 11, "chain": 12}[kind])
-    for T in (1, 2, 5, 17, 64):
+    for T in (1, 2, 5, 17, 64, 65, 130):
         for _ in range(20):
             parents = make_tree_parents(rng, T, kind)
             if T > 3 and rng.random() < 0.3:      # plant an invalid parent
@@ -88,7 +88,7 @@ def test_capi_argument_checks(B):
     fake = 1 << 20  # never dereferenced: every call below fails validation first
     args = dict(tree_parents=fake, draft_tokens=fake, target_tokens=fake, root_targets=fake, batch=2,
                 tree_nodes=16, accept_len=fake, accept_path=fake, bonus_token=fake, stream=0)
-    for over in (dict(batch=0), dict(tree_nodes=0), dict(tree_nodes=65), dict(draft_tokens=0),
+    for over in (dict(batch=0), dict(tree_nodes=0), dict(tree_nodes=257), dict(draft_tokens=0),
                  dict(accept_path=0)):
         with pytest.raises(B.MlaVerifyError) as e:
             B.mla_tree_accept(**{**args, **over})

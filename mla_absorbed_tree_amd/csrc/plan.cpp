@@ -55,10 +55,16 @@ double estimate_launch(const std::vector<int64_t>& tiles, const std::vector<int6
 // k = 1, 2, ..., no shorter than kMinChunkTiles (a split's partial costs
 // about a few tiles); S_b = ceil(tiles_b / chunk). The estimate decides; a
 // candidate must beat the best so far by 1% (ties keep fewer splits).
+// Shorter chunks only add workgroups, so the search stops at the first
+// candidate with more than kMaxSearchWorkgroups of them (beyond one split per
+// sequence): by then the chip runs many even rounds and finer chunks buy
+// little, while each estimate costs time in proportion to the workgroups.
 std::vector<int32_t> choose_auto_splits(const std::vector<int64_t>& tiles,
                                         const std::vector<int64_t>& row_blocks, int rows_per_block, int dtype) {
   constexpr int64_t kMinChunkTiles = 8;
   constexpr int64_t kMaxCandidates = 512;
+  constexpr int64_t kMaxSearchWorkgroups = 16 * kComputeUnits;
+  int64_t first_n = -1;
   const int64_t max_tiles = tiles.empty() ? 0 : *std::max_element(tiles.begin(), tiles.end());
   std::vector<int32_t> best(tiles.size(), 0), cand(tiles.size(), 0);
   double best_t = -1.0;
@@ -70,8 +76,13 @@ std::vector<int32_t> choose_auto_splits(const std::vector<int64_t>& tiles,
       continue;
     }
     last_chunk = chunk;
-    for (size_t b = 0; b < tiles.size(); ++b)
+    int64_t n = 0;
+    for (size_t b = 0; b < tiles.size(); ++b) {
       cand[b] = tiles[b] > 0 ? int32_t(std::max<int64_t>(1, (tiles[b] + chunk - 1) / chunk)) : 0;
+      n += int64_t(cand[b]) * row_blocks[b];
+    }
+    if (first_n < 0) first_n = n;
+    else if (n > first_n + kMaxSearchWorkgroups) break;
     const double t = estimate_launch(tiles, row_blocks, cand, rows_per_block, dtype);
     if (best_t < 0.0 || t < 0.99 * best_t) {
       best_t = t;

@@ -160,3 +160,13 @@ def test_ragged_tree_plans(B):
         assert B.mla_verify_plan_get_info(a) == B.mla_verify_plan_get_info(b) and wa == wb
         B.mla_verify_plan_destroy(a)
         B.mla_verify_plan_destroy(b)
+
+
+def test_planning_large_batches_is_fast(B):
+    """The automatic split search stays cheap for big batches of long sequences."""
+    import time
+    for b, h, t, n in ((256, 64, 64, 200000), (256, 1, 1, 200000), (1, 64, 256, 200256)):
+        t0 = time.perf_counter()
+        p, _ = B.mla_verify_plan(b, h, t, 1, [n] * b)
+        assert time.perf_counter() - t0 < 0.5, (b, h, t, n)
+        B.mla_verify_plan_destroy(p)

@@ -15,12 +15,13 @@ from gen import get_config, make_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _setup(name, **over):
+def _setup(name, tree_lens=None, **over):
     from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
     cfg = get_config(name, **over)
-    x = make_inputs(cfg)
+    x = make_inputs(cfg, tree_lens=tree_lens)
     d = device_inputs(x)
-    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, cfg.num_splits)
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, cfg.num_splits,
+                   tree_lens=tree_lens)
     return cfg, x, d, mv
 
 
@@ -28,11 +29,15 @@ def _setup(name, **over):
     ("b1_h64_p4096_t16_bf16", dict(prefix=1000, batch=2)),            # split: attention + combine
     ("b1_h64_p4096_t16_bf16", dict(prefix=1000, batch=2, num_splits=1)),  # one split: attention only
     ("tiny_f32_b1_h16_p256_t8", {}),
+    # packed trees of 200, 0 and 70 nodes: the workgroup mask builder, idle row blocks
+    ("b1_h64_p4096_t16_bf16", dict(prefix=500, batch=3, heads=16, tree_nodes=200,
+                                   tree_lens=[200, 0, 70])),
+    ("tiny_f32_b1_h16_p256_t8", dict(batch=2, heads=4, tree_nodes=130, tree_lens=[130, 65])),
 ])
 def test_graph_replays_match_eager(name, over):
     cfg, x, d, mv = _setup(name, **over)
     args = [d[k] for k in ("q_nope", "q_pe", "kv_c", "k_pe", "kv_indptr", "kv_indices", "tree_parents")]
-    rows = cfg.batch * cfg.tree_nodes
+    rows = int(x.tree_indptr[-1])
     out = torch.empty((rows, cfg.heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((rows, cfg.heads), dtype=torch.float32, device="cuda")
 

@@ -172,3 +172,13 @@ def test_ragged_long_prefixes_sampled():
     rows = node_rows(x, nodes)
     compare(o[rows], lse[rows], o_ref, lse_ref, "bf16", "plan=%s" % info)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("dtype,splits", [("bf16", 0), ("bf16", 3), ("f32", 0)])
+def test_max_batch(dtype, splits):
+    """256 sequences (the batch limit): every offset table of the launch at full
+    length; tree sizes 0..9 and prefixes 0..300, all rows against the oracle."""
+    cfg = get_config("b8_h64_paged600k_t16_bf16", batch=256, heads=4, tree_nodes=9,
+                     tree_range=(0, 9), prefix_range=(0, 300), pool_slots=45000, dtype=dtype,
+                     seed=50)
+    _full(cfg, splits, poison_unused=True)

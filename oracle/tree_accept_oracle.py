@@ -68,3 +68,23 @@ def tree_accept_batch(parents: np.ndarray, draft: np.ndarray, target: np.ndarray
         lens[b], bonus[b] = n, tok
         paths[b, :n] = path
     return lens, paths, bonus
+
+
+def tree_accept_packed(parents: np.ndarray, draft: np.ndarray, target: np.ndarray,
+                       root_target: np.ndarray, tree_indptr: np.ndarray):
+    """Packed trees: sequence b owns nodes tree_indptr[b] .. tree_indptr[b+1]-1
+    of the flat parents / draft / target arrays (parents are node indices of
+    the same tree). Returns (accept_len [B], accept_path [sum T_b] where
+    sequence b's path starts at tree_indptr[b] and is padded with -1 to T_b,
+    bonus_token [B])."""
+    ind = [int(v) for v in np.asarray(tree_indptr)]
+    B = len(ind) - 1
+    lens = np.zeros(B, np.int32)
+    paths = np.full(ind[-1], -1, np.int32)
+    bonus = np.zeros(B, np.int32)
+    for b in range(B):
+        lo, hi = ind[b], ind[b + 1]
+        n, path, tok = tree_accept(parents[lo:hi], draft[lo:hi], target[lo:hi], int(root_target[b]))
+        lens[b], bonus[b] = n, tok
+        paths[lo:lo + n] = path
+    return lens, paths, bonus

@@ -93,3 +93,31 @@ def test_capi_argument_checks(B):
         with pytest.raises(B.MlaVerifyError) as e:
             B.mla_tree_accept(**{**args, **over})
         assert e.value.status == B.MLA_ERR_INVALID_ARG, over
+
+
+def test_packed_trees_match_per_sequence_results():
+    """Packed layout: each sequence's slice gives exactly the single-tree
+    result (checked by the brute force), including empty trees; with equal
+    sizes the packed result is the uniform batch result flattened."""
+    from oracle import tree_accept_batch, tree_accept_packed
+    rng = np.random.default_rng(77)
+    sizes = [5, 0, 70, 1, 130, 0, 17]
+    trees = [make_tree_parents(rng, T, "uniform") for T in sizes]
+    toks = [make_accept_tokens(rng, p, vocab=3, p_match=0.85) for p in trees]
+    ind = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    flat = lambda k: np.concatenate([t[k] for t in toks]).astype(np.int32)
+    parents = np.concatenate(trees).astype(np.int32)
+    root = np.array([t[2] for t in toks], np.int32)
+    lens, paths, bonus = tree_accept_packed(parents, flat(0), flat(1), root, ind)
+    for b, T in enumerate(sizes):
+        n, path, tok = _brute_force(trees[b], toks[b][0], toks[b][1], toks[b][2])
+        assert (lens[b], bonus[b]) == (n, tok), b
+        assert list(paths[ind[b]:ind[b] + n]) == path and (paths[ind[b] + n:ind[b + 1]] == -1).all()
+    # equal sizes: same as the uniform batch layout
+    P = np.stack([make_tree_parents(rng, 9, "bounded") for _ in range(4)]).astype(np.int32)
+    tk = [make_accept_tokens(rng, P[b], vocab=3, p_match=0.85) for b in range(4)]
+    d, t, r = (np.stack([x[0] for x in tk]), np.stack([x[1] for x in tk]), np.array([x[2] for x in tk]))
+    u = tree_accept_batch(P, d, t, r)
+    k = tree_accept_packed(P.reshape(-1), d.reshape(-1), t.reshape(-1), r, np.arange(5) * 9)
+    for a, c in zip(u, k):
+        np.testing.assert_array_equal(a.reshape(-1), c)

@@ -59,6 +59,34 @@ mla_status mla_tree_accept(const int32_t* tree_parents, const int32_t* draft_tok
                            int32_t tree_nodes, int32_t* accept_len, int32_t* accept_path,
                            int32_t* bonus_token, void* stream);
 
+/*
+ * The same acceptance over packed trees, one size per sequence (the layout of
+ * mla_verify_run with tree_len_host): sequence b owns nodes
+ * tree_indptr[b] .. tree_indptr[b+1]-1 of the flat arrays.
+ *   tree_indptr    device int32 [batch+1], tree_indptr[0] = 0, non-decreasing
+ *   tree_parents, draft_tokens, target_tokens
+ *                  device int32 [tree_indptr[batch]]; parents are node indices
+ *                  of the same tree (-1 = child of the last prefix token)
+ *   root_targets   device int32 [batch]
+ *   max_tree_nodes 0..MLA_TREE_ACCEPT_MAX_TREE, at least every T_b; sizes the
+ *                  launch (64 lanes per sequence up to 64, else 256)
+ *   accept_len     device int32 [batch], written; -1 marks a sequence whose
+ *                  size read on the device lies outside 0..max_tree_nodes (its
+ *                  path slots are then not written)
+ *   accept_path    device int32 [tree_indptr[batch]], written: sequence b's
+ *                  path from its root down at tree_indptr[b], then -1 up to T_b
+ *   bonus_token    device int32 [batch], written (root_targets[b] for an empty
+ *                  tree or a rejected size)
+ * The rule, conventions and errors are those of mla_tree_accept. An empty tree
+ * accepts nothing (accept_len 0). The arrays of the nodes may be NULL when
+ * max_tree_nodes is 0.
+ */
+mla_status mla_tree_accept_packed(const int32_t* tree_parents, const int32_t* draft_tokens,
+                                  const int32_t* target_tokens, const int32_t* root_targets,
+                                  const int32_t* tree_indptr, int32_t batch, int32_t max_tree_nodes,
+                                  int32_t* accept_len, int32_t* accept_path, int32_t* bonus_token,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_r
                     "mla_verify_attend", "mla_verify_combine",
                     "mla_verify_tree_masks", "mla_verify_plan_destroy",
                     "mla_verify_status_string", "mla_verify_last_error", "mla_kv_compact",
-                    "mla_tree_accept")
+                    "mla_tree_accept", "mla_tree_accept_packed")
 
 
 class MlaVerifyError(RuntimeError):
@@ -74,13 +74,15 @@ def _load():
     lib.mla_verify_plan_destroy.argtypes = [vp]
     lib.mla_kv_compact.argtypes = [i32, i32, i64, vp, vp, i64, i64, vp, vp, vp, vp, i64, i64, i32, vp, vp]
     lib.mla_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
+    lib.mla_tree_accept_packed.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
     lib.mla_verify_status_string.argtypes = [i32]
     lib.mla_verify_status_string.restype = ctypes.c_char_p
     lib.mla_verify_last_error.argtypes = []
     lib.mla_verify_last_error.restype = ctypes.c_char_p
     for name in ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
                  "mla_verify_attend", "mla_verify_combine", "mla_verify_tree_masks",
-                 "mla_verify_plan_destroy", "mla_kv_compact", "mla_tree_accept"):
+                 "mla_verify_plan_destroy", "mla_kv_compact", "mla_tree_accept",
+                 "mla_tree_accept_packed"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -214,3 +216,12 @@ def mla_tree_accept(tree_parents, draft_tokens, target_tokens, root_targets, bat
     _check(_lib.mla_tree_accept(_ptr(tree_parents), _ptr(draft_tokens), _ptr(target_tokens),
                                 _ptr(root_targets), int(batch), int(tree_nodes), _ptr(accept_len),
                                 _ptr(accept_path), _ptr(bonus_token), _stream_handle(stream)))
+
+
+def mla_tree_accept_packed(tree_parents, draft_tokens, target_tokens, root_targets, tree_indptr,
+                           batch: int, max_tree_nodes: int, accept_len, accept_path, bonus_token,
+                           stream=None) -> None:
+    _check(_lib.mla_tree_accept_packed(_ptr(tree_parents), _ptr(draft_tokens), _ptr(target_tokens),
+                                       _ptr(root_targets), _ptr(tree_indptr), int(batch),
+                                       int(max_tree_nodes), _ptr(accept_len), _ptr(accept_path),
+                                       _ptr(bonus_token), _stream_handle(stream)))

@@ -243,8 +243,27 @@ mla_status mla_tree_accept(const int32_t* tree_parents, const int32_t* draft_tok
   if (batch < 1 || tree_nodes < 1 || tree_nodes > MLA_TREE_ACCEPT_MAX_TREE)
     return fail(MLA_ERR_INVALID_ARG,
                 "batch must be >= 1 and tree_nodes in 1.." + std::to_string(MLA_TREE_ACCEPT_MAX_TREE));
-  const int e = mlav::launch_tree_accept(tree_parents, draft_tokens, target_tokens, root_targets, batch,
-                                         tree_nodes, accept_len, accept_path, bonus_token, stream);
+  const int e = mlav::launch_tree_accept(tree_parents, draft_tokens, target_tokens, root_targets, nullptr,
+                                         batch, tree_nodes, accept_len, accept_path, bonus_token, stream);
+  if (e != 0) return fail(MLA_ERR_HIP, "tree acceptance launch failed (hipError " + std::to_string(e) + ")");
+  return MLA_OK;
+}
+
+mla_status mla_tree_accept_packed(const int32_t* tree_parents, const int32_t* draft_tokens,
+                                  const int32_t* target_tokens, const int32_t* root_targets,
+                                  const int32_t* tree_indptr, int32_t batch, int32_t max_tree_nodes,
+                                  int32_t* accept_len, int32_t* accept_path, int32_t* bonus_token,
+                                  void* stream) {
+  g_last_error.clear();
+  if (!tree_indptr || !root_targets || !accept_len || !bonus_token)
+    return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
+  if (max_tree_nodes > 0 && (!tree_parents || !draft_tokens || !target_tokens || !accept_path))
+    return fail(MLA_ERR_INVALID_ARG, "NULL device pointer");
+  if (batch < 1 || max_tree_nodes < 0 || max_tree_nodes > MLA_TREE_ACCEPT_MAX_TREE)
+    return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 and max_tree_nodes in 0.." +
+                                         std::to_string(MLA_TREE_ACCEPT_MAX_TREE));
+  const int e = mlav::launch_tree_accept(tree_parents, draft_tokens, target_tokens, root_targets, tree_indptr,
+                                         batch, max_tree_nodes, accept_len, accept_path, bonus_token, stream);
   if (e != 0) return fail(MLA_ERR_HIP, "tree acceptance launch failed (hipError " + std::to_string(e) + ")");
   return MLA_OK;
 }

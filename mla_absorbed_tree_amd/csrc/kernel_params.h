@@ -45,8 +45,9 @@ int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks,
 int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream);
 int launch_tree_masks(const int32_t* parents, int32_t batch, int32_t tree_nodes, uint64_t* masks,
                       void* stream);  // masks [batch, tree_nodes, ceil(tree_nodes / 64)]
+// indptr NULL: trees of T nodes each; else packed trees of at most T nodes.
 int launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target,
-                       const int32_t* root_target, int32_t batch, int32_t T, int32_t* accept_len,
-                       int32_t* accept_path, int32_t* bonus, void* stream);
+                       const int32_t* root_target, const int32_t* indptr, int32_t batch, int32_t T,
+                       int32_t* accept_len, int32_t* accept_path, int32_t* bonus, void* stream);
 
 }  // namespace mlav

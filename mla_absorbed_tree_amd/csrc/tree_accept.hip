@@ -1,6 +1,7 @@
-// Greedy token acceptance over a verified draft tree: one 64-lane wave per
-// sequence with one tree node per lane for trees of up to 64 nodes, one
-// 256-lane workgroup above that. Acceptance of a node is the AND of a local
+// Greedy token acceptance over verified draft trees (one tree per sequence,
+// of a uniform size or packed with a size each): one 64-lane wave per tree
+// with one node per lane for trees of up to 64 nodes, one 256-lane workgroup
+// above that. Acceptance of a node is the AND of a local
 // test (its draft token equals the target's token after its parent) over its
 // ancestor-or-self set, which the shared pointer-doubling mask gives directly:
 // accepted(t) = (anc(t) & ~ok) == 0.
@@ -12,24 +13,25 @@
 
 namespace mlav {
 
-__global__ void __launch_bounds__(64) mla_tree_accept_kernel(const int32_t* __restrict__ parents,
-                                                             const int32_t* __restrict__ draft,
-                                                             const int32_t* __restrict__ target,
-                                                             const int32_t* __restrict__ root_target, int T,
-                                                             int32_t* __restrict__ accept_len,
-                                                             int32_t* __restrict__ accept_path,
-                                                             int32_t* __restrict__ bonus) {
-  const int b = blockIdx.x;
+// Outputs of one sequence: its accept_len / bonus slots and its path row.
+struct AcceptOut {
+  int32_t* len;
+  int32_t* bonus;
+  int32_t* path;  // T entries
+};
+
+// Trees of up to 64 nodes: one wave, one node per lane (lanes >= T idle).
+__device__ __forceinline__ void wave_accept(const int32_t* __restrict__ par_b, const int32_t* __restrict__ draft_b,
+                                            const int32_t* __restrict__ target_b, int root_tok, int T,
+                                            const AcceptOut& o) {
   const int lane = lane_id();
   const bool live = lane < T;
-  const int64_t base = (int64_t)b * T;
-  const uint64_t anc = wave_tree_mask(parents + base, T);
-  const int root_tok = root_target[b];
+  const uint64_t anc = wave_tree_mask(par_b, T);
   bool ok = false;
   if (live && anc != 0) {
-    const int par = parents[base + lane];
-    const int want = par < 0 ? root_tok : target[base + par];
-    ok = draft[base + lane] == want;
+    const int par = par_b[lane];
+    const int want = par < 0 ? root_tok : target_b[par];
+    ok = draft_b[lane] == want;
   }
   const uint64_t ok_mask = __ballot(ok);
   const bool accepted = live && anc != 0 && (anc & ~ok_mask) == 0;
@@ -39,11 +41,11 @@ __global__ void __launch_bounds__(64) mla_tree_accept_kernel(const int32_t* __re
   int key = accepted ? depth * 64 + (63 - lane) : -1;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) key = max(key, shfl_i32(key, lane ^ off));
-  if (live) accept_path[base + lane] = -1;
+  if (live) o.path[lane] = -1;
   if (key < 0) {
     if (lane == 0) {
-      accept_len[b] = 0;
-      bonus[b] = root_tok;
+      *o.len = 0;
+      *o.bonus = root_tok;
     }
     return;
   }
@@ -54,10 +56,10 @@ __global__ void __launch_bounds__(64) mla_tree_accept_kernel(const int32_t* __re
   // same lane, or on another lane whose slot this lane does not write.
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  if (live && ((path >> lane) & 1ull)) accept_path[base + depth - 1] = lane;
+  if (live && ((path >> lane) & 1ull)) o.path[depth - 1] = lane;
   if (lane == 0) {
-    accept_len[b] = len;
-    bonus[b] = target[base + best];
+    *o.len = len;
+    *o.bonus = target_b[best];
   }
 }
 
@@ -65,21 +67,19 @@ __global__ void __launch_bounds__(64) mla_tree_accept_kernel(const int32_t* __re
 // workgroup builder (kMaskWords words per node, zero on an invalid chain);
 // each wave's ballot of the local test is one word of the OK mask. The
 // deepest accepted node wins (smallest index among equals), and every slot of
-// the path row is written exactly once, from the path gathered in LDS.
+// the path row is written exactly once, from the path gathered in LDS. Every
+// thread of the kMaxTreeNodes-lane workgroup must call it.
 constexpr int kAcceptThreads = kMaxTreeNodes;
-__global__ void __launch_bounds__(kAcceptThreads) mla_tree_accept_large_kernel(
-    const int32_t* __restrict__ parents, const int32_t* __restrict__ draft, const int32_t* __restrict__ target,
-    const int32_t* __restrict__ root_target, int T, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ accept_path, int32_t* __restrict__ bonus) {
+__device__ __forceinline__ void block_accept(const int32_t* __restrict__ par_b, const int32_t* __restrict__ draft_b,
+                                             const int32_t* __restrict__ target_b, int root_tok, int T,
+                                             const AcceptOut& o) {
   __shared__ __attribute__((aligned(16))) char scratch[kTreeScratchBytes];
   __shared__ uint64_t ok_words[kMaskWords];
   __shared__ int wave_key[kAcceptThreads / 64];
   __shared__ int path_lds[kMaxTreeNodes];
-  const int b = blockIdx.x;
   const int t = threadIdx.x, wave = t >> 6;
   const bool live = t < T;
-  const int64_t base = (int64_t)b * T;
-  block_tree_masks<kAcceptThreads>(parents + base, T, scratch);
+  block_tree_masks<kAcceptThreads>(par_b, T, scratch);
   const uint64_t* anc = tree_scratch_masks(scratch) + t * kMaskWords;
   uint64_t any = 0;
   int depth = 0;
@@ -90,12 +90,11 @@ __global__ void __launch_bounds__(kAcceptThreads) mla_tree_accept_large_kernel(
       depth += __popcll(anc[w]);
     }
   }
-  const int root_tok = root_target[b];
   bool ok = false;
   if (live && any != 0) {
-    const int par = parents[base + t];
-    const int want = par < 0 ? root_tok : target[base + par];
-    ok = draft[base + t] == want;
+    const int par = par_b[t];
+    const int want = par < 0 ? root_tok : target_b[par];
+    ok = draft_b[t] == want;
   }
   const uint64_t ballot = __ballot(ok);
   if ((t & 63) == 0) ok_words[wave] = ballot;
@@ -123,23 +122,58 @@ __global__ void __launch_bounds__(kAcceptThreads) mla_tree_accept_large_kernel(
     if ((pm[t >> 6] >> (t & 63)) & 1ull) path_lds[depth - 1] = t;
   }
   __syncthreads();
-  if (live) accept_path[base + t] = t < len ? path_lds[t] : -1;
+  if (live) o.path[t] = t < len ? path_lds[t] : -1;
   if (t == 0) {
-    accept_len[b] = len;
-    bonus[b] = best < 0 ? root_tok : target[base + best];
+    *o.len = len;
+    *o.bonus = best < 0 ? root_tok : target_b[best];
   }
 }
 
+// One workgroup per sequence. Sequence b's tree is nodes base .. base+T-1 of
+// the flat arrays: base = b * T_uniform without `indptr`, else
+// indptr[b] .. indptr[b+1]-1. A packed size outside 0..max_T (or a negative
+// offset) gives accept_len = -1 and bonus = root_target, and writes no path.
+// Launched with 64 lanes when max_T <= 64, else kAcceptThreads.
+template <int kThreadsN>
+__global__ void __launch_bounds__(kThreadsN) mla_tree_accept_kernel(
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ draft, const int32_t* __restrict__ target,
+    const int32_t* __restrict__ root_target, const int32_t* __restrict__ indptr, int T_uniform, int max_T,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_path, int32_t* __restrict__ bonus) {
+  const int b = blockIdx.x;
+  int64_t base = (int64_t)b * T_uniform;
+  int T = T_uniform;
+  if (indptr) {
+    base = indptr[b];
+    T = indptr[b + 1] - indptr[b];
+  }
+  const int root_tok = root_target[b];
+  if (base < 0 || T < 0 || T > max_T) {
+    if (threadIdx.x == 0) {
+      accept_len[b] = -1;
+      bonus[b] = root_tok;
+    }
+    return;
+  }
+  const AcceptOut o{accept_len + b, bonus + b, accept_path + base};
+  if (T <= 64) {
+    if (threadIdx.x < 64) wave_accept(parents + base, draft + base, target + base, root_tok, T, o);
+    return;
+  }
+  if constexpr (kThreadsN >= kAcceptThreads) block_accept(parents + base, draft + base, target + base, root_tok, T, o);
+}
+
 int launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target,
-                       const int32_t* root_target, int32_t batch, int32_t T, int32_t* accept_len,
-                       int32_t* accept_path, int32_t* bonus, void* stream) {
+                       const int32_t* root_target, const int32_t* indptr, int32_t batch, int32_t T,
+                       int32_t* accept_len, int32_t* accept_path, int32_t* bonus, void* stream) {
+  const int T_uniform = indptr ? 0 : T;
   if (T <= 64)
-    hipLaunchKernelGGL(mla_tree_accept_kernel, dim3((unsigned)batch), dim3(64), 0, (hipStream_t)stream, parents,
-                       draft, target, root_target, (int)T, accept_len, accept_path, bonus);
-  else
-    hipLaunchKernelGGL(mla_tree_accept_large_kernel, dim3((unsigned)batch), dim3(kAcceptThreads), 0,
-                       (hipStream_t)stream, parents, draft, target, root_target, (int)T, accept_len, accept_path,
+    hipLaunchKernelGGL(mla_tree_accept_kernel<64>, dim3((unsigned)batch), dim3(64), 0, (hipStream_t)stream,
+                       parents, draft, target, root_target, indptr, T_uniform, (int)T, accept_len, accept_path,
                        bonus);
+  else
+    hipLaunchKernelGGL(mla_tree_accept_kernel<kAcceptThreads>, dim3((unsigned)batch), dim3(kAcceptThreads), 0,
+                       (hipStream_t)stream, parents, draft, target, root_target, indptr, T_uniform, (int)T,
+                       accept_len, accept_path, bonus);
   return (int)hipGetLastError();
 }
 

@@ -93,6 +93,14 @@ def test_capi_argument_checks(B):
         with pytest.raises(B.MlaVerifyError) as e:
             B.mla_tree_accept(**{**args, **over})
         assert e.value.status == B.MLA_ERR_INVALID_ARG, over
+    packed = dict(tree_parents=fake, draft_tokens=fake, target_tokens=fake, root_targets=fake,
+                  tree_indptr=fake, batch=2, max_tree_nodes=16, accept_len=fake, accept_path=fake,
+                  bonus_token=fake, stream=0)
+    for over in (dict(batch=0), dict(max_tree_nodes=-1), dict(max_tree_nodes=257), dict(tree_indptr=0),
+                 dict(draft_tokens=0), dict(bonus_token=0)):
+        with pytest.raises(B.MlaVerifyError) as e:
+            B.mla_tree_accept_packed(**{**packed, **over})
+        assert e.value.status == B.MLA_ERR_INVALID_ARG, over
 
 
 def test_packed_trees_match_per_sequence_results():

@@ -207,33 +207,52 @@ def bench_kv_compact(steps, warmup, name="b8_h64_paged600k_t16_bf16"):
             "verify_step_ms_scattered": t_scattered, "verify_step_ms_compacted": t_compacted}
 
 
-def bench_tree_accept(steps, warmup, batch=8, tree_nodes=16, seed=7):
+def bench_tree_accept(steps, warmup, batch=8, tree_nodes=16, seed=7, packed_sizes=(172, 207, 6, 207)):
     """Token acceptance after the verify step (one launch per decode step) on
-    synthetic draft/target tokens: its average launch time."""
+    synthetic draft/target tokens: average launch time for `batch` trees of
+    `tree_nodes` nodes, and for packed trees of the ragged workload's sizes
+    (the 256-lane path)."""
     import torch
     from gen import make_accept_tokens, make_tree_parents
     from mla_absorbed_tree_amd import binding as B
 
     rng = np.random.default_rng(seed)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps * 1e3
+
     parents = np.stack([make_tree_parents(rng, tree_nodes, "uniform") for _ in range(batch)])
     toks = [make_accept_tokens(rng, parents[b]) for b in range(batch)]
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
     args = (dev(parents), dev(np.stack([t[0] for t in toks])), dev(np.stack([t[1] for t in toks])),
             dev(np.array([t[2] for t in toks])), batch, tree_nodes,
             torch.empty(batch, dtype=torch.int32, device="cuda"),
             torch.empty((batch, tree_nodes), dtype=torch.int32, device="cuda"),
             torch.empty(batch, dtype=torch.int32, device="cuda"))
-    for _ in range(warmup):
-        B.mla_tree_accept(*args)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    ev[0].record()
-    for _ in range(steps):
-        B.mla_tree_accept(*args)
-    ev[1].record()
-    torch.cuda.synchronize()
-    return {"batch": batch, "tree_nodes": tree_nodes, "us_per_launch": ev[0].elapsed_time(ev[1]) / steps * 1e3,
-            "bound": "launch latency (one wave per sequence)"}
+    us = timed(lambda: B.mla_tree_accept(*args))
+
+    trees = [make_tree_parents(rng, int(T), "uniform") for T in packed_sizes]
+    ptoks = [make_accept_tokens(rng, p) for p in trees]
+    ind = np.concatenate([[0], np.cumsum(packed_sizes)])
+    nb = len(packed_sizes)
+    pargs = (dev(np.concatenate(trees)), dev(np.concatenate([t[0] for t in ptoks])),
+             dev(np.concatenate([t[1] for t in ptoks])), dev(np.array([t[2] for t in ptoks])), dev(ind), nb,
+             int(max(packed_sizes)), torch.empty(nb, dtype=torch.int32, device="cuda"),
+             torch.empty(int(ind[-1]), dtype=torch.int32, device="cuda"),
+             torch.empty(nb, dtype=torch.int32, device="cuda"))
+    us_packed = timed(lambda: B.mla_tree_accept_packed(*pargs))
+    return {"batch": batch, "tree_nodes": tree_nodes, "us_per_launch": us,
+            "packed": {"tree_sizes": [int(t) for t in packed_sizes], "us_per_launch": us_packed},
+            "bound": "launch latency (one wave, or one 256-lane workgroup, per sequence)"}
 
 
 def kernel_source_digest():

@@ -170,3 +170,24 @@ def test_planning_large_batches_is_fast(B):
         p, _ = B.mla_verify_plan(b, h, t, 1, [n] * b)
         assert time.perf_counter() - t0 < 0.5, (b, h, t, n)
         B.mla_verify_plan_destroy(p)
+
+
+def test_plans_of_the_named_workloads(B):
+    """The planner's choices for the measured workloads (a change here changes
+    what the benchmark measures, so it should be deliberate)."""
+    from gen import get_config, make_inputs
+    want = {"tiny_f32_b1_h16_p256_t8": (2, 32, 1), "b1_h64_p4096_t16_bf16": (17, 192, 1),
+            "b4_h64_p32768_t64_bf16": (8, 256, 1), "b1_h64_p200000_t32_bf16_s256": (256, 256, 16),
+            "b8_h64_paged600k_t16_bf16": (92, 768, 1), "b4_h64_p32768_t1to256_ragged_bf16": (32, 3328, 1)}
+    for name, (splits, grid, group) in want.items():
+        cfg = get_config(name)
+        rng = np.random.default_rng(cfg.seed)  # only the lengths and tree sizes are needed
+        P = (rng.integers(*cfg.prefix_range, size=cfg.batch, endpoint=True) if cfg.prefix_range
+             else np.full(cfg.batch, cfg.prefix))
+        Tb = rng.integers(*cfg.tree_range, size=cfg.batch, endpoint=True) if cfg.tree_range else None
+        kv = P + (Tb if Tb is not None else cfg.tree_nodes)
+        p, _ = B.mla_verify_plan(cfg.batch, cfg.heads, cfg.tree_nodes, 1 if cfg.dtype == "bf16" else 0, kv,
+                                 cfg.num_splits, tree_len_host=Tb)
+        info = B.mla_verify_plan_get_info(p)
+        B.mla_verify_plan_destroy(p)
+        assert (info["total_splits"], info["grid_blocks"], info["splits_per_workgroup"]) == (splits, grid, group), name

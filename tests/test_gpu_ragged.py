@@ -182,3 +182,20 @@ def test_max_batch(dtype, splits):
                      tree_range=(0, 9), prefix_range=(0, 300), pool_slots=45000, dtype=dtype,
                      seed=50)
     _full(cfg, splits, poison_unused=True)
+
+
+def test_ragged_bench_workload_sampled():
+    """The benchmark's packed-tree workload at full size and in its launch
+    configuration (automatic splits): sampled nodes, on both sides of the
+    64-node mask word boundary, against the oracle."""
+    cfg = get_config("b4_h64_p32768_t1to256_ragged_bf16")
+    x = make_inputs(cfg)
+    Tb = [int(t) for t in x.tree_lens]
+    nodes = [(b, t) for b in range(cfg.batch) for t in sorted({0, 63, 64, 127, 128, Tb[b] - 1}) if t < Tb[b]]
+    log("case %s tree_lens=%s (sampled %d nodes)" % (cfg.name, Tb, len(nodes)))
+    o, lse, info = run_hip(x, 0)
+    assert info["total_splits"] == 32, info
+    o_ref, lse_ref = run_oracle(x, nodes=nodes)
+    rows = node_rows(x, nodes)
+    compare(o[rows], lse[rows], o_ref, lse_ref, "bf16", "plan=%s" % info)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()

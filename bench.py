@@ -117,7 +117,8 @@ def bench_workload(name, steps, warmup, num_splits=None):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    attn_each = [e[0].elapsed_time(e[1]) for e in events]
+    attn_ms = float(np.mean(attn_each))
     comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     step_ms = wall / steps * 1e3
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
@@ -131,7 +132,8 @@ def bench_workload(name, steps, warmup, num_splits=None):
         "hbm_gbps": bytes_ / (step_ms * 1e-3) / 1e9,
         "hbm_frac": bytes_ / (step_ms * 1e-3) / PEAK_HBM_BYTES,
         "mfma_frac": flops / (step_ms * 1e-3) / PEAK_BF16_FLOPS,
-        "kernels_ms": {"attention": attn_ms, "combine": comb_ms},
+        "kernels_ms": {"attention": attn_ms, "combine": comb_ms,
+                       "attention_median": float(np.median(attn_each))},
         "plan": mv.info,
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS, "traffic": measured_traffic(name),
@@ -282,9 +284,10 @@ def measured_traffic(workload):
     return None if w is None or "traffic_bytes" not in w else float(w["traffic_bytes"])
 
 
-def cpu_baseline(x, budget_s=15.0):
+def cpu_baseline(x, budget_s=15.0, single_budget_s=5.0):
     """Time the float64 oracle on a bounded sample of the workload's nodes and
-    scale to the whole step (KV tokens/s)."""
+    scale to the whole step (KV tokens/s), with the host's BLAS threads and
+    again with one thread (a smaller sample)."""
     from oracle import verify_attention
     try:
         from threadpoolctl import threadpool_info
@@ -304,10 +307,21 @@ def cpu_baseline(x, budget_s=15.0):
     n = int(min(len(order), max(1, budget_s / max(first, 1e-3))))
     took = run(order[:n])
     full = took / n * len(order)
-    return {"value": float(x.kv_lens.sum()) / full, "unit": "KV tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": "%d of %d tree nodes (all %d heads each) of %s in %.1f s; full step "
-                      "extrapolated to %.1f s" % (n, len(order), cfg.heads, cfg.name, took, full)}
+    res = {"value": float(x.kv_lens.sum()) / full, "unit": "KV tokens/s", "cores": int(cores),
+           "kind": "oracle",
+           "sample": "%d of %d tree nodes (all %d heads each) of %s in %.1f s; full step "
+                     "extrapolated to %.1f s" % (n, len(order), cfg.heads, cfg.name, took, full)}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = run(order[:1])
+            n1 = int(min(len(order), max(1, single_budget_s / max(one, 1e-3))))
+            took1 = run(order[:n1])
+        res["one_thread"] = {"value": float(x.kv_lens.sum()) / (took1 / n1 * len(order)),
+                             "sample": "%d tree nodes in %.1f s" % (n1, took1)}
+    except ImportError:
+        pass
+    return res
 
 
 def main():

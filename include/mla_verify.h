@@ -147,6 +147,25 @@ mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void
                           void* stream);
 
 /*
+ * mla_verify_run with the tree packing read on the device, so that one plan
+ * (or one captured graph) serves decode steps whose tree sizes change:
+ *   tree_indptr device int32 [batch+1]: sequence b's nodes are packed nodes
+ *               tree_indptr[b] .. tree_indptr[b+1]-1 of q_nope, q_pe,
+ *               tree_parents, out and lse (sized for tree_indptr[batch] nodes).
+ *               Its size T_b must lie in 0..the plan's size for b (its
+ *               tree_len_host entry, or tree_nodes), which fixes the row
+ *               blocks. A sequence whose size or offset is out of range is
+ *               skipped: none of its rows are written.
+ * Every other argument, the NaN rule for invalid parents and the capture
+ * rules are those of mla_verify_run.
+ */
+mla_status mla_verify_run_varlen(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                                 const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* tree_indptr,
+                                 const int32_t* tree_parents, float scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The two halves of mla_verify_run, for callers that schedule or time them
  * separately. mla_verify_attend takes exactly the arguments of mla_verify_run
  * and enqueues the attention kernel: sequences with one KV split write out/lse

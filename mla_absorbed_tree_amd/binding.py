@@ -28,6 +28,7 @@ MLA_TREE_ACCEPT_MAX_TREE = 256
 
 # Symbols declared in include/*.h.
 EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
+                    "mla_verify_run_varlen",
                     "mla_verify_attend", "mla_verify_combine",
                     "mla_verify_tree_masks", "mla_verify_plan_destroy",
                     "mla_verify_status_string", "mla_verify_last_error", "mla_kv_compact",
@@ -69,6 +70,8 @@ def _load():
     lib.mla_verify_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                    ctypes.c_size_t, vp]
     lib.mla_verify_attend.argtypes = lib.mla_verify_run.argtypes
+    lib.mla_verify_run_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                          ctypes.c_size_t, vp]
     lib.mla_verify_combine.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.mla_verify_tree_masks.argtypes = [vp, i32, i32, vp, vp]
     lib.mla_verify_plan_destroy.argtypes = [vp]
@@ -79,7 +82,7 @@ def _load():
     lib.mla_verify_status_string.restype = ctypes.c_char_p
     lib.mla_verify_last_error.argtypes = []
     lib.mla_verify_last_error.restype = ctypes.c_char_p
-    for name in ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
+    for name in ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run", "mla_verify_run_varlen",
                  "mla_verify_attend", "mla_verify_combine", "mla_verify_tree_masks",
                  "mla_verify_plan_destroy", "mla_kv_compact", "mla_tree_accept",
                  "mla_tree_accept_packed"):
@@ -171,6 +174,18 @@ def mla_verify_run(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_p
                                _ptr(kv_indptr), _ptr(kv_indices), _ptr(tree_parents),
                                float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                int(workspace_bytes), _stream_handle(stream)))
+
+
+def mla_verify_run_varlen(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_indptr,
+                          tree_parents, scale: float, out, lse, workspace,
+                          workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """mla_verify_run with the tree packing read from the device tree_indptr [batch+1]."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.mla_verify_run_varlen(plan, _ptr(q_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe),
+                                      _ptr(kv_indptr), _ptr(kv_indices), _ptr(tree_indptr),
+                                      _ptr(tree_parents), float(scale), _ptr(out), _ptr(lse),
+                                      _ptr(workspace), int(workspace_bytes), _stream_handle(stream)))
 
 
 def mla_verify_attend(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents,

@@ -72,7 +72,8 @@ namespace {
 mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe, const void* kv_c,
                    const void* k_pe, const int32_t* kv_indptr, const int32_t* kv_indices,
                    const int32_t* tree_parents, float scale, float* out, float* lse,
-                   void* workspace, size_t workspace_bytes, bool need_inputs, mlav::VerifyArgs& a) {
+                   void* workspace, size_t workspace_bytes, bool need_inputs, mlav::VerifyArgs& a,
+                   const int32_t* tree_indptr = nullptr) {
   if (!plan) return fail(MLA_ERR_INVALID_ARG, "plan is NULL");
   const mlav::Plan& p = plan->plan;
   // A batch without any tree node has no query rows: its q, parent and output
@@ -100,6 +101,7 @@ mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
   a.kv_indptr = kv_indptr;
   a.kv_indices = kv_indices;
   a.parents = tree_parents;
+  a.tree_indptr = tree_indptr;
   a.out = out;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
@@ -147,6 +149,22 @@ mla_status mla_verify_run(mla_verify_plan_t plan, const void* q_nope, const void
   mlav::VerifyArgs a;
   mla_status st = prepare(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents, scale,
                           out, lse, workspace, workspace_bytes, true, a);
+  if (st != MLA_OK) return st;
+  st = launch_attend(plan->plan, a, stream);
+  if (st != MLA_OK) return st;
+  return launch_combine(plan->plan, a, stream);
+}
+
+mla_status mla_verify_run_varlen(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                                 const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                                 const int32_t* kv_indices, const int32_t* tree_indptr,
+                                 const int32_t* tree_parents, float scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!tree_indptr) return fail(MLA_ERR_INVALID_ARG, "tree_indptr is NULL");
+  mlav::VerifyArgs a;
+  mla_status st = prepare(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents, scale,
+                          out, lse, workspace, workspace_bytes, true, a, tree_indptr);
   if (st != MLA_OK) return st;
   st = launch_attend(plan->plan, a, stream);
   if (st != MLA_OK) return st;

@@ -18,6 +18,10 @@ struct VerifyArgs {
   const int32_t* kv_indptr;    // [B + 1]
   const int32_t* kv_indices;   // page table, page_size = 1
   const int32_t* parents;      // [nodes], node indices local to the sequence
+  // Device tree offsets [B + 1] read at run time, or nullptr (node_offset
+  // below). Sequence b's device size must lie in 0..its planned size
+  // node_offset[b+1] - node_offset[b]; a sequence outside that is skipped.
+  const int32_t* tree_indptr;
   float* out;                  // [nodes, H, 512]
   float* lse;                  // [nodes, H] or nullptr
   // Split partials [total_splits, part_rows, 512] (split launches only):

@@ -138,6 +138,20 @@ struct BlockWork {
 // First key tile of split s of a sequence with ntiles tiles and S splits.
 __device__ __forceinline__ int split_tile(int s, int ntiles, int S) { return (int)(((int64_t)s * ntiles) / S); }
 
+// First packed node and size of sequence b's tree: the plan's packing, or the
+// device offsets of a run that reads them (a size outside 0..the planned size,
+// or a negative offset, gives an empty tree: the sequence is skipped).
+__device__ __forceinline__ void seq_tree(const VerifyArgs& a, int b, int& node0, int& T) {
+  node0 = a.node_offset[b];
+  T = a.node_offset[b + 1] - node0;
+  if (a.tree_indptr) {
+    const int cap = T;
+    node0 = a.tree_indptr[b];
+    T = a.tree_indptr[b + 1] - node0;
+    if (node0 < 0 || T < 0 || T > cap) T = 0;
+  }
+}
+
 // Returns false for a workgroup with nothing to do: past the last split group,
 // or a row block past its sequence's T_b * H rows (row blocks are counted for
 // the largest tree; smaller trees leave the rest idle).
@@ -155,8 +169,7 @@ __device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w, int
     else hi = mid - 1;
   }
   w.b = lo;
-  w.node0 = a.node_offset[w.b];
-  w.T = a.node_offset[w.b + 1] - w.node0;
+  seq_tree(a, w.b, w.node0, w.T);
   w.rows = w.T * a.heads;
   if (w.rb * rows_per_block >= w.rows) return false;
   w.S = a.split_offset[w.b + 1] - a.split_offset[w.b];
@@ -1052,8 +1065,9 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   __shared__ f32x4_t accsh[kCombineRows][kCombineGroups - 1][32][4];
   const int row_groups = (a.max_rows_per_seq + kCombineRows - 1) / kCombineRows;
   const int b = (int)(blockIdx.x / row_groups);
-  const int node0 = a.node_offset[b];
-  const int rows = (a.node_offset[b + 1] - node0) * a.heads;
+  int node0, T;
+  seq_tree(a, b, node0, T);
+  const int rows = T * a.heads;
   const int tid = threadIdx.x;
   const int j = tid / (32 * kCombineGroups), grp = (tid >> 5) % kCombineGroups, t32 = tid & 31;
   const int r = (int)(blockIdx.x % row_groups) * kCombineRows + j;

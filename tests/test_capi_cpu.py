@@ -191,3 +191,13 @@ def test_plans_of_the_named_workloads(B):
         info = B.mla_verify_plan_get_info(p)
         B.mla_verify_plan_destroy(p)
         assert (info["total_splits"], info["grid_blocks"], info["splits_per_workgroup"]) == (splits, grid, group), name
+
+
+def test_varlen_run_requires_tree_indptr(B):
+    p, ws = B.mla_verify_plan(2, 4, 8, 1, [100, 50], tree_len_host=[8, 3])
+    fake = 1 << 20  # never dereferenced: the call fails validation first
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_run_varlen(p, fake, fake, fake, fake, fake, fake, 0, fake, 0.1, fake, fake, fake, ws,
+                                stream=0)
+    assert e.value.status == B.MLA_ERR_INVALID_ARG
+    B.mla_verify_plan_destroy(p)

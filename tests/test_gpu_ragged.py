@@ -199,3 +199,128 @@ def test_ragged_bench_workload_sampled():
     rows = node_rows(x, nodes)
     compare(o[rows], lse[rows], o_ref, lse_ref, "bf16", "plan=%s" % info)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+# --------------------------------------------------------------------------
+# tree sizes read on the device (mla_verify_run_varlen)
+# --------------------------------------------------------------------------
+
+def _dev(a, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return (t.to(dtype) if dtype is not None else t).cuda()
+
+
+@pytest.mark.parametrize("dtype,splits", [("bf16", 0), ("bf16", 3), ("f32", 0)])
+def test_varlen_sizes_below_plan_bounds(dtype, splits):
+    import torch
+    from mla_absorbed_tree_amd import binding as B
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+    cfg = get_config("b1_h64_p4096_t16_bf16", batch=3, heads=8, tree_nodes=200, prefix=300, dtype=dtype,
+                     seed=51)
+    x = make_inputs(cfg, tree_lens=[150, 0, 10])          # this step's trees
+    bounds = [200, 64, 10]                                # the plan's per-sequence bounds
+    d = device_inputs(x)
+    mv = MlaVerify(3, 8, 200, dtype, np.asarray(x.prefix_lens) + np.asarray(bounds), splits, tree_lens=bounds)
+    nodes = int(x.tree_indptr[-1])
+    out = torch.full((nodes, 8, 512), 7.0, device="cuda")
+    lse = torch.full((nodes, 8), 7.0, device="cuda")
+    B.mla_verify_run_varlen(mv.plan, d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"],
+                            d["kv_indices"], _dev(x.tree_indptr), d["tree_parents"], x.scale, out, lse,
+                            mv.workspace)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = run_oracle(x)
+    compare(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dtype, "plan=%s" % mv.info)
+    mv.close()
+
+
+def test_varlen_size_past_bound_is_skipped():
+    import torch
+    from mla_absorbed_tree_amd import binding as B
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+    cfg = get_config("b1_h64_p4096_t16_bf16", batch=2, heads=8, tree_nodes=12, prefix=90, seed=52)
+    x = make_inputs(cfg, tree_lens=[12, 5])
+    d = device_inputs(x)
+    mv = MlaVerify(2, 8, 12, "bf16", np.asarray(x.prefix_lens) + 10, 2, tree_lens=[10, 10])
+    out = torch.full((17, 8, 512), 7.0, device="cuda")
+    lse = torch.full((17, 8), 7.0, device="cuda")
+    B.mla_verify_run_varlen(mv.plan, d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"],
+                            d["kv_indices"], _dev(x.tree_indptr), d["tree_parents"], x.scale, out, lse,
+                            mv.workspace)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    assert (o[:12] == 7.0).all() and (l[:12] == 7.0).all()      # 12 > bound 10: not written
+    nodes = [(1, t) for t in range(5)]
+    o_ref, lse_ref = run_oracle(x, nodes=nodes)
+    compare(o[12:], l[12:], o_ref, lse_ref, "bf16")
+    mv.close()
+
+
+def test_varlen_graph_serves_steps_with_changing_tree_sizes():
+    """One plan and one captured graph; two decode steps whose tree sizes,
+    trees, key lengths, page tables and queries are rewritten in place on the
+    device. Each replay matches the oracle for its own step."""
+    import torch
+    from mla_absorbed_tree_amd import binding as B
+    from mla_absorbed_tree_amd.verify import MlaVerify
+    H, bounds = 16, [128, 70]
+    steps = [make_inputs(get_config("b1_h64_p4096_t16_bf16", batch=2, heads=H, tree_nodes=128, prefix=400,
+                                    seed=53 + k), tree_lens=tl, prefix_lens=pl)
+             for k, (tl, pl) in enumerate((([100, 70], [400, 650]), ([128, 3], [700, 380])))]
+    cap_nodes = max(int(x.tree_indptr[-1]) for x in steps)
+    cap_keys = max(int(x.kv_indptr[-1]) for x in steps)
+    bf = torch.bfloat16
+    qn = torch.zeros((cap_nodes, H, 512), dtype=bf, device="cuda")
+    qp = torch.zeros((cap_nodes, H, 64), dtype=bf, device="cuda")
+    kc = torch.zeros((cap_keys, 512), dtype=bf, device="cuda")
+    kp = torch.zeros((cap_keys, 64), dtype=bf, device="cuda")
+    kv_indptr = torch.zeros(3, dtype=torch.int32, device="cuda")
+    kv_indices = torch.zeros(cap_keys, dtype=torch.int32, device="cuda")
+    tree_indptr = torch.zeros(3, dtype=torch.int32, device="cuda")
+    parents = torch.zeros(cap_nodes, dtype=torch.int32, device="cuda")
+    out = torch.zeros((cap_nodes, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((cap_nodes, H), dtype=torch.float32, device="cuda")
+    plan_lens = [max(int(x.kv_lens[b]) for x in steps) for b in range(2)]
+    mv = MlaVerify(2, H, 128, "bf16", plan_lens, 0, tree_lens=bounds)
+
+    def load(x):
+        n, k = int(x.tree_indptr[-1]), int(x.kv_indptr[-1])
+        qn[:n].copy_(_dev(x.q_nope, bf))
+        qp[:n].copy_(_dev(x.q_pe, bf))
+        kc[:k].copy_(_dev(x.kv_c, bf))
+        kp[:k].copy_(_dev(x.k_pe, bf))
+        kv_indptr.copy_(_dev(x.kv_indptr))
+        kv_indices[:k].copy_(_dev(x.kv_indices))
+        tree_indptr.copy_(_dev(x.tree_indptr))
+        parents[:n].copy_(_dev(x.parents))
+        torch.cuda.synchronize()
+
+    def call():
+        B.mla_verify_run_varlen(mv.plan, qn, qp, kc, kp, kv_indptr, kv_indices, tree_indptr, parents,
+                                steps[0].scale, out, lse, mv.workspace)
+
+    load(steps[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for x in steps:
+            load(x)
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            n = int(x.tree_indptr[-1])
+            o_ref, lse_ref = run_oracle(x)
+            compare(out[:n].cpu().numpy(), lse[:n].cpu().numpy(), o_ref, lse_ref, "bf16",
+                    "replay %d tree sizes %s" % (rep, list(x.tree_lens)))
+    del g
+    mv.close()

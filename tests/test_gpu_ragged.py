@@ -324,3 +324,36 @@ def test_varlen_graph_serves_steps_with_changing_tree_sizes():
                     "replay %d tree sizes %s" % (rep, list(x.tree_lens)))
     del g
     mv.close()
+
+
+def test_random_shapes_sweep():
+    """Randomly drawn small problems (fixed seed), every element against the
+    oracle: 1..16 heads (odd counts included), prefixes of 0..400 keys, tree
+    sizes 0..256 per sequence, three tree kinds, paged or contiguous KV,
+    bf16 and fp32, automatic or forced splits."""
+    rng = np.random.default_rng(60)
+    for case in range(24):
+        dtype = "bf16" if case % 3 else "f32"
+        batch = int(rng.integers(1, 6))
+        heads = int(rng.choice([1, 3, 5, 8, 16]))
+        tmax = int(rng.choice([1, 7, 64, 65, 130, 256]))
+        tree_lens = rng.integers(0, tmax + 1, size=batch)
+        tree_lens[int(rng.integers(0, batch))] = tmax
+        prefix = rng.integers(0, 401, size=batch)
+        kind = str(rng.choice(["uniform", "bounded", "chain"]))
+        paged = bool(rng.integers(0, 2))
+        splits = int(rng.choice([0, 0, 1, 2, 5]))
+        total = int((prefix + tree_lens).sum())
+        over = dict(batch=batch, heads=heads, tree_nodes=tmax, dtype=dtype, tree_kind=kind,
+                    max_depth=300, max_branch=3, seed=1000 + case)
+        if paged:
+            cfg = get_config("b8_h64_paged600k_t16_bf16", prefix_range=(0, 1), pool_slots=total + 37, **over)
+        else:
+            cfg = get_config("b1_h64_p4096_t16_bf16", prefix=0, **over)
+        x = make_inputs(cfg, tree_lens=tree_lens, prefix_lens=prefix, poison_unused=paged)
+        log("sweep case %d: %s H=%d T_b=%s P=%s %s splits=%d %s" % (case, dtype, heads, list(tree_lens),
+                                                                     list(prefix), kind, splits,
+                                                                     "paged" if paged else "contiguous"))
+        o, lse, info = run_hip(x, splits)
+        o_ref, lse_ref = run_oracle(x)
+        compare(o, lse, o_ref, lse_ref, dtype, "plan=%s" % info)

@@ -257,12 +257,15 @@ def test_varlen_size_past_bound_is_skipped():
 
 
 def test_varlen_graph_serves_steps_with_changing_tree_sizes():
-    """One plan and one captured graph; two decode steps whose tree sizes,
-    trees, key lengths, page tables and queries are rewritten in place on the
-    device. Each replay matches the oracle for its own step."""
+    """One plan and one captured graph holding a decode step's verify attention
+    and token acceptance; two steps whose tree sizes, trees, key lengths, page
+    tables, queries and (synthetic) tokens are rewritten in place on the
+    device. Each replay matches the oracles for its own step."""
     import torch
+    from gen import make_accept_tokens
     from mla_absorbed_tree_amd import binding as B
     from mla_absorbed_tree_amd.verify import MlaVerify
+    from oracle import tree_accept_packed
     H, bounds = 16, [128, 70]
     steps = [make_inputs(get_config("b1_h64_p4096_t16_bf16", batch=2, heads=H, tree_nodes=128, prefix=400,
                                     seed=53 + k), tree_lens=tl, prefix_lens=pl)
@@ -282,9 +285,26 @@ def test_varlen_graph_serves_steps_with_changing_tree_sizes():
     lse = torch.zeros((cap_nodes, H), dtype=torch.float32, device="cuda")
     plan_lens = [max(int(x.kv_lens[b]) for x in steps) for b in range(2)]
     mv = MlaVerify(2, H, 128, "bf16", plan_lens, 0, tree_lens=bounds)
+    trng = np.random.default_rng(59)
+    tokens = []
+    for x in steps:
+        per = [make_accept_tokens(trng, x.parents[x.tree_indptr[b]:x.tree_indptr[b + 1]], vocab=3, p_match=0.85)
+               for b in range(2)]
+        tokens.append((np.concatenate([t[0] for t in per]).astype(np.int32),
+                       np.concatenate([t[1] for t in per]).astype(np.int32),
+                       np.array([t[2] for t in per], np.int32)))
+    draft = torch.zeros(cap_nodes, dtype=torch.int32, device="cuda")
+    target = torch.zeros(cap_nodes, dtype=torch.int32, device="cuda")
+    root = torch.zeros(2, dtype=torch.int32, device="cuda")
+    acc_len = torch.zeros(2, dtype=torch.int32, device="cuda")
+    acc_path = torch.zeros(cap_nodes, dtype=torch.int32, device="cuda")
+    bonus = torch.zeros(2, dtype=torch.int32, device="cuda")
 
-    def load(x):
+    def load(x, tok):
         n, k = int(x.tree_indptr[-1]), int(x.kv_indptr[-1])
+        draft[:n].copy_(_dev(tok[0]))
+        target[:n].copy_(_dev(tok[1]))
+        root.copy_(_dev(tok[2]))
         qn[:n].copy_(_dev(x.q_nope, bf))
         qp[:n].copy_(_dev(x.q_pe, bf))
         kc[:k].copy_(_dev(x.kv_c, bf))
@@ -298,8 +318,9 @@ def test_varlen_graph_serves_steps_with_changing_tree_sizes():
     def call():
         B.mla_verify_run_varlen(mv.plan, qn, qp, kc, kp, kv_indptr, kv_indices, tree_indptr, parents,
                                 steps[0].scale, out, lse, mv.workspace)
+        B.mla_tree_accept_packed(parents, draft, target, root, tree_indptr, 2, 128, acc_len, acc_path, bonus)
 
-    load(steps[0])
+    load(steps[0], tokens[0])
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -311,9 +332,11 @@ def test_varlen_graph_serves_steps_with_changing_tree_sizes():
         call()
     torch.cuda.synchronize()
     for rep in range(2):
-        for x in steps:
-            load(x)
+        for x, tok in zip(steps, tokens):
+            load(x, tok)
             out.fill_(float("nan"))
+            acc_len.fill_(-5)
+            acc_path.fill_(-5)
             lse.fill_(float("nan"))
             torch.cuda.synchronize()
             g.replay()
@@ -322,6 +345,10 @@ def test_varlen_graph_serves_steps_with_changing_tree_sizes():
             o_ref, lse_ref = run_oracle(x)
             compare(out[:n].cpu().numpy(), lse[:n].cpu().numpy(), o_ref, lse_ref, "bf16",
                     "replay %d tree sizes %s" % (rep, list(x.tree_lens)))
+            want = tree_accept_packed(x.parents, tok[0], tok[1], tok[2], x.tree_indptr)
+            got = (acc_len.cpu().numpy(), acc_path[:n].cpu().numpy(), bonus.cpu().numpy())
+            for g_, w_, name in zip(got, want, ("accept_len", "accept_path", "bonus_token")):
+                np.testing.assert_array_equal(g_, w_, err_msg="replay %d %s" % (rep, name))
     del g
     mv.close()
 

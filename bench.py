@@ -358,8 +358,9 @@ def main():
     if not a.no_also and a.workload == PRIMARY:
         for name in (ALSO, RAGGED):
             r2, _ = bench_workload(name, a.steps, a.warmup)
-            also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "hbm_gbps", "hbm_frac",
-                                            "mfma_frac", "kernels_ms", "roofline", "config", "plan")})
+            also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "visible_pairs_per_s",
+                                            "hbm_gbps", "hbm_frac", "mfma_frac", "kernels_ms", "roofline",
+                                            "config", "plan")})
     compact = accept = None
     if not a.no_also and not a.no_compact:
         compact = bench_kv_compact(a.steps, a.warmup)
@@ -383,6 +384,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": res["config"],
+        "visible_pairs_per_s": res["visible_pairs_per_s"],
         "hbm_gbps": res["hbm_gbps"],
         "hbm_frac": res["hbm_frac"],
         "mfma_frac": res["mfma_frac"],

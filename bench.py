@@ -349,7 +349,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 3}))
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
         sys.exit(2)
 

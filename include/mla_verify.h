@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = -1, /* bad size, NULL pointer, misaligned stride ... */
-  MLA_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement */
+  MLA_ERR_UNSUPPORTED = -2, /* a valid request the library does not implement */
   MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the plan needs */
   MLA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } mla_status;

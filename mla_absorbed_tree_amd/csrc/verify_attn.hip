@@ -360,19 +360,27 @@ __device__ __forceinline__ void issue_tile(const TileLoads& t, int wave) {
 // stop the compiler from hoisting every read at once. between(kb) runs after
 // the MFMAs of batch kb.
 constexpr int kQkRopeBatch = 0;
-template <typename Between>
+// With kQpePreloaded the caller has already read the rope part of Q into
+// qf_pre (the tile loop reads it across its barrier); otherwise qf_pre is
+// unused and it is read here.
+template <bool kQpePreloaded, typename Between>
 __device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qreg)[32], const char* qpe, int k_off,
-                                            int kpe_off, int kpe_sw, int half, Between&& between) {
+                                            int kpe_off, int kpe_sw, int half, const bf16x8_t (&qf_pre)[4],
+                                            Between&& between) {
   f32x16_t sacc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
   bf16x8_t kf[2][4], qf[4];
+  if constexpr (kQpePreloaded) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qf[j] = qf_pre[j];
+  }
   auto load_batch = [&](int b, bf16x8_t (&dst)[4]) {
     if (b == kQkRopeBatch) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         dst[j] = *(const bf16x8_t*)(buf + kpe_off + (((2 * j + half) ^ kpe_sw) << 4));
-        qf[j] = *(const bf16x8_t*)(qpe + j * 64 * 16);
+        if constexpr (!kQpePreloaded) qf[j] = *(const bf16x8_t*)(qpe + j * 64 * 16);
       }
     } else {
       const int c0 = 4 * (b < kQkRopeBatch ? b : b - 1);
@@ -703,7 +711,9 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       wait_vmem<kVmemPerTile + 1>();  // this wave's part of tile tb
       block_sync();
       {
-        f32x16_t s0 = qk_tile(smem + (tb % kNbuf) * kBufBytes, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half, [](int) {});
+        bf16x8_t qf_none[4];
+        f32x16_t s0 = qk_tile<false>(smem + (tb % kNbuf) * kBufBytes, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half,
+                                     qf_none, [](int) {});
         if (needs_mask(tb * kKeysPerTile)) mask_tile(s0, tb * kKeysPerTile);
         softmax_to_lds(s0, pbuf0 + (tb & 1) * kPBytes, overflow);
       }
@@ -729,6 +739,12 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         if (tile == split_begin && sp != s_first) wait_vmem<kPartialStores>();
         else wait_vmem<0>();
         wait_lds();
+        // The rope part of Q is this lane's own LDS data, written once before
+        // the loop, so its reads may cross the barrier: the batch that follows
+        // it then waits for the key reads alone (measured 0.5-1.3% faster).
+        bf16x8_t qf_pre[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qf_pre[j] = *(const bf16x8_t*)(qpe_lane + j * 64 * 16);
         block_sync();  // P(tile) and tile+1 are visible; every wave has finished PV(tile-1)
         // Tile+2 goes into the buffer tile-1 used; its addresses were prepared
         // during the previous iteration. One load goes after each QK batch (a
@@ -766,7 +782,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         const int k1 = (tile + 1) * kKeysPerTile;
         const bool has_next = tile + 1 < te;
         if (has_next) {
-          snext = qk_tile(smem + bo1, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half, late_part);
+          snext = qk_tile<true>(smem + bo1, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half, qf_pre, late_part);
         } else {
           issue_tile(pending, wave);
           issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);

@@ -1,8 +1,9 @@
 """GPU parity: libmlaverify (HIP, gfx950) against the float64 oracle.
 
-Small cases compare every output element; the three large workloads compare
-sampled tree nodes (all heads, all 512 features) that the oracle computes one
-by one, plus size-independent properties (split invariance, determinism).
+Small cases compare every output element. The three large workloads are
+compared in full (every node, head and feature) and on sampled tree nodes
+that the oracle computes one by one, plus size-independent properties (split
+invariance, determinism).
 """
 import numpy as np
 import pytest
@@ -213,6 +214,20 @@ def test_b1_p200000_t32_s256_sampled():
 def test_b8_paged600k_sampled():
     _sampled("b8_h64_paged600k_t16_bf16", [(0, 3), (2, 15), (4, 0), (5, 9), (7, 12)],
              poison_unused=True)
+
+
+@pytest.mark.parametrize("name", ["b4_h64_p32768_t64_bf16", "b1_h64_p200000_t32_bf16_s256",
+                                  "b8_h64_paged600k_t16_bf16"])
+def test_full_size_every_node(name):
+    """The large workloads at full size in the benchmark's launch configuration
+    (the workload's own split setting), every output element against the
+    oracle; the paged pool's unused slots hold NaN."""
+    cfg = get_config(name)
+    x = make_inputs(cfg, poison_unused=cfg.layout == "paged")
+    log("case %s (every node)" % name)
+    o, lse, info = run_hip(x, cfg.num_splits)
+    o_ref, lse_ref = run_oracle(x)
+    compare(o, lse, o_ref, lse_ref, cfg.dtype, "plan=%s" % info)
 
 
 def test_split_invariance_at_full_size():

@@ -217,7 +217,7 @@ def test_b8_paged600k_sampled():
 
 
 @pytest.mark.parametrize("name", ["b4_h64_p32768_t64_bf16", "b1_h64_p200000_t32_bf16_s256",
-                                  "b8_h64_paged600k_t16_bf16"])
+                                  "b8_h64_paged600k_t16_bf16", "b4_h64_p32768_t1to256_ragged_bf16"])
 def test_full_size_every_node(name):
     """The large workloads at full size in the benchmark's launch configuration
     (the workload's own split setting), every output element against the

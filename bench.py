@@ -9,8 +9,8 @@ of synthetic inputs that already sit in HBM. The primary workload is the
 compaction of the paged workload's 600k-slot pool (its kernel's HBM rate, and
 the verify step on the scattered against the compacted pool) in "kv_compact",
 and the token-acceptance launch that follows a verify step in "tree_accept".
-A batch of packed trees of 1..256 nodes per sequence (32k prefix) is reported in
-"also" as well.
+The paged workload (page_size = 1 pool of 600k slots) and a batch of packed
+trees of 1..256 nodes per sequence (32k prefix) are reported in "also" as well.
 
 Prints ONE JSON line. `value` is KV tokens/s (sum of N_b per step / step time);
 `roofline` describes the attention kernel (algorithmic FLOPs per launch over
@@ -36,6 +36,7 @@ PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
 PRIMARY = "b4_h64_p32768_t64_bf16"
 ALSO = "b1_h64_p200000_t32_bf16_s256"
 RAGGED = "b4_h64_p32768_t1to256_ragged_bf16"
+PAGED = "b8_h64_paged600k_t16_bf16"
 
 
 def log(msg):
@@ -356,7 +357,7 @@ def main():
     res, x = bench_workload(a.workload, a.steps, a.warmup, a.num_splits)
     also = []
     if not a.no_also and a.workload == PRIMARY:
-        for name in (ALSO, RAGGED):
+        for name in (ALSO, PAGED, RAGGED):
             r2, _ = bench_workload(name, a.steps, a.warmup)
             also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "visible_pairs_per_s",
                                             "hbm_gbps", "hbm_frac", "mfma_frac", "kernels_ms", "roofline",

@@ -71,8 +71,9 @@ mla_status mla_tree_accept(const int32_t* tree_parents, const int32_t* draft_tok
  *   max_tree_nodes 0..MLA_TREE_ACCEPT_MAX_TREE, at least every T_b; sizes the
  *                  launch (64 lanes per sequence up to 64, else 256)
  *   accept_len     device int32 [batch], written; -1 marks a sequence whose
- *                  size read on the device lies outside 0..max_tree_nodes (its
- *                  path slots are then not written)
+ *                  device entries are out of range: a size outside
+ *                  0..max_tree_nodes, a negative offset, or a tree that ends
+ *                  past tree_indptr[batch] (its path slots are then not written)
  *   accept_path    device int32 [tree_indptr[batch]], written: sequence b's
  *                  path from its root down at tree_indptr[b], then -1 up to T_b
  *   bonus_token    device int32 [batch], written (root_targets[b] for an empty

@@ -70,16 +70,34 @@ typedef struct {
   const int32_t* tree_len_host; /* host [batch]: T_b, the tree nodes of sequence b, each in
                                    0..tree_nodes (0: the sequence has no query this step),
                                    or NULL: every sequence has tree_nodes nodes. Read during
-                                   the call only; fixed for the plan's runs. The pages give
-                                   the verify kernel a set of query nodes, the tree's
-                                   leaves and internal nodes, with no bound on their
-                                   number ["Ground Truth in Silicon" page, "Input
-                                   Knowledge Required", item 3]. */
+                                   the call only; fixed for the plan's runs. Every node
+                                   of the draft tree is a query of the verify step, and
+                                   the pages put no limit on how many there are ["Ground
+                                   Truth in Silicon" page, "Input Knowledge Required",
+                                   item 3]. */
 } mla_verify_problem;
 
+/* The batch bound comes from kernel-argument space: the per-sequence split,
+   split-group and node offset tables (3 x (batch + 1) int32) travel in each
+   launch's argument block, whose size the launch limits to 4 KB. */
 #define MLA_VERIFY_MAX_BATCH 256
 /* Ancestor masks are four 64-bit words per node. */
 #define MLA_VERIFY_MAX_TREE 256
+
+/* Per-sequence status words: int32 [batch] at byte offset 0 of the workspace,
+   written by the device on every run that has at least one tree node
+   (mla_verify_run, mla_verify_run_varlen, mla_verify_attend); 0 = the
+   sequence's tree and lengths are valid, else an OR of these bits.  They are
+   stored with plain vector stores, never cleared in between, so capturing a
+   run in a graph captures them too. */
+#define MLA_VERIFY_STATUS_BAD_PARENT 1 /* a parent outside -1..node-1: the rows of
+                                           every node whose ancestor chain meets it
+                                           are NaN (out and lse) */
+#define MLA_VERIFY_STATUS_SHORT_KV 2   /* N_b < T_b on the device: every row of the
+                                           sequence is NaN */
+#define MLA_VERIFY_STATUS_TREE_RANGE 4 /* mla_verify_run_varlen: tree_indptr entries
+                                           out of range; no row of the sequence is
+                                           written */
 
 typedef struct {
   int32_t total_splits;     /* sum over sequences of the KV splits */
@@ -133,10 +151,15 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
  *   out         device fp32 [nodes, H, 512]
  *   lse         device fp32 [nodes, H] (natural log) or NULL
  *   workspace   device, >= workspace_bytes of the plan, 256-byte aligned.  Holds
- *               split partials between the two launches; concurrent runs need
- *               separate workspaces.
- * No allocation, no host synchronisation and no host reads of device data:
- * the call only enqueues kernels, so it can be captured in a HIP graph.
+ *               the status words (MLA_VERIFY_STATUS_*, int32 [batch] at offset
+ *               0) and the split partials between the two launches; concurrent
+ *               runs need separate workspaces.
+ * No allocation, no host synchronisation, no memset and no host reads of
+ * device data: the call only enqueues kernels, so it can be captured in a HIP
+ * graph and replayed across decode steps (the pages' verify kernel was made
+ * capture-safe for the serving loop's CUDA-graph capture: "The
+ * Information-Gathering Pivot" page, "Input Knowledge and Assumptions" and
+ * "The Significance of the Transition").
  * A plan whose trees are all empty (nodes = 0) enqueues nothing; q_nope, q_pe,
  * tree_parents, out and lse may then be NULL.
  */

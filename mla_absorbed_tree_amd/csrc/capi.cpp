@@ -107,6 +107,7 @@ mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
   char* ws = static_cast<char*>(workspace);
   a.part_o = p.combine ? static_cast<void*>(ws + p.ws_part_o) : nullptr;
   a.part_ml = p.combine ? reinterpret_cast<float*>(ws + p.ws_part_ml) : nullptr;
+  a.status = reinterpret_cast<int32_t*>(ws + p.ws_status);
   a.kv_c_stride = p.kv_c_stride;
   a.k_pe_stride = p.k_pe_stride;
   a.scale_log2 = scale * 1.4426950408889634f;

@@ -29,6 +29,7 @@ struct VerifyArgs {
   // bf16 problems. Rows past a sequence's T_b * H are padding (never read).
   void* part_o;
   float* part_ml;              // [total_splits, part_rows, 2]  (m in log2 units, l)
+  int32_t* status;             // [batch] per-sequence status words (MLA_VERIFY_STATUS_*)
   int64_t kv_c_stride;         // elements
   int64_t k_pe_stride;         // elements
   float scale_log2;            // softmax scale * log2(e)
@@ -38,6 +39,9 @@ struct VerifyArgs {
   int32_t part_rows;           // row_blocks * rows per workgroup (>= max_rows_per_seq)
   int32_t row_blocks;          // workgroups along the rows of the largest tree
   int32_t total_splits;
+  // The per-sequence tables travel in the kernel-argument block (three
+  // tables of MLA_VERIFY_MAX_BATCH + 1 words, about 3 KB of the 4 KB that a
+  // launch's arguments may take), which is what bounds the batch.
   int32_t split_offset[MLA_VERIFY_MAX_BATCH + 1];  // first global split of sequence b
   int32_t group;                                   // consecutive splits per workgroup
   int32_t group_offset[MLA_VERIFY_MAX_BATCH + 1];  // first split group of sequence b

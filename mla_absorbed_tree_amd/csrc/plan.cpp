@@ -221,8 +221,9 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
     return MLA_ERR_UNSUPPORTED;
   }
 
-  size_t off = 256;  // status flags live in the first 256 bytes
+  // The per-sequence status words come first, then the split partials.
   plan.ws_status = 0;
+  size_t off = align_up(size_t(p.batch) * sizeof(int32_t), 256);
   if (plan.combine) {
     // Partial rows per split padded to whole row blocks (the bf16 kernel
     // stores unconditionally, padding rows included).

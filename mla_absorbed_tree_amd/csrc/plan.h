@@ -41,7 +41,7 @@ struct Plan {
   int64_t grid_blocks = 0;      // attention launch
   bool combine = false;         // some sequence has S_b > 1
   // Workspace layout (byte offsets from the workspace start).
-  size_t ws_status = 0;         // int32 status flags
+  size_t ws_status = 0;         // int32 [batch] status words (MLA_VERIFY_STATUS_*)
   // Per (split, row), rows padded to row_blocks * rows_per_block per split:
   size_t ws_part_ml = 0;        // float2 (m in log2 units, l)
   size_t ws_part_o = 0;         // [512] unnormalised O: fp32, or bf16 for bf16 problems

@@ -131,8 +131,9 @@ __device__ __forceinline__ void block_accept(const int32_t* __restrict__ par_b, 
 
 // One workgroup per sequence. Sequence b's tree is nodes base .. base+T-1 of
 // the flat arrays: base = b * T_uniform without `indptr`, else
-// indptr[b] .. indptr[b+1]-1. A packed size outside 0..max_T (or a negative
-// offset) gives accept_len = -1 and bonus = root_target, and writes no path.
+// indptr[b] .. indptr[b+1]-1. A packed size outside 0..max_T, a negative
+// offset, or a tree that ends past indptr[batch] gives accept_len = -1 and
+// bonus = root_target, and writes no path.
 // Launched with 64 lanes when max_T <= 64, else kAcceptThreads.
 template <int kThreadsN>
 __global__ void __launch_bounds__(kThreadsN) mla_tree_accept_kernel(
@@ -147,7 +148,10 @@ __global__ void __launch_bounds__(kThreadsN) mla_tree_accept_kernel(
     T = indptr[b + 1] - indptr[b];
   }
   const int root_tok = root_target[b];
-  if (base < 0 || T < 0 || T > max_T) {
+  // The packed tree must also end inside the node arrays, which hold
+  // indptr[batch] nodes.
+  const bool past_end = indptr && base + T > (int64_t)indptr[gridDim.x];
+  if (base < 0 || T < 0 || T > max_T || past_end) {
     if (threadIdx.x == 0) {
       accept_len[b] = -1;
       bonus[b] = root_tok;

@@ -35,6 +35,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 #include "kernel_params.h"
 #include "wave_tree.h"
@@ -95,6 +97,17 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
+// f(std::integral_constant<int, I>) for I = 0..N-1, as straight-line code:
+// every index is a compile-time constant, whatever the size of the body.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Ancestor masks of sequence blockIdx.x's tree, masks[(b*T + t) * W + w] with
 // W = ceil(T / 64): the one-wave builder for T <= 64 (the first wave), the
 // workgroup builder above, as in the attention kernels.
@@ -133,29 +146,37 @@ struct BlockWork {
   int kv0, N, P, ntiles;
   int tile_begin, tile_end;   // key tiles of the whole group
   bool seq_ok;
+  int tree_status;            // MLA_VERIFY_STATUS_TREE_RANGE or 0 (seq_tree)
 };
 
 // First key tile of split s of a sequence with ntiles tiles and S splits.
 __device__ __forceinline__ int split_tile(int s, int ntiles, int S) { return (int)(((int64_t)s * ntiles) / S); }
 
 // First packed node and size of sequence b's tree: the plan's packing, or the
-// device offsets of a run that reads them (a size outside 0..the planned size,
-// or a negative offset, gives an empty tree: the sequence is skipped).
-__device__ __forceinline__ void seq_tree(const VerifyArgs& a, int b, int& node0, int& T) {
+// device offsets of a run that reads them. Device entries out of range (a size
+// outside 0..the planned size, a negative offset, or a tree ending past
+// tree_indptr[batch]) give an empty tree, so the sequence is skipped, and
+// return MLA_VERIFY_STATUS_TREE_RANGE; otherwise 0.
+__device__ __forceinline__ int seq_tree(const VerifyArgs& a, int b, int& node0, int& T) {
   node0 = a.node_offset[b];
   T = a.node_offset[b + 1] - node0;
   if (a.tree_indptr) {
     const int cap = T;
     node0 = a.tree_indptr[b];
     T = a.tree_indptr[b + 1] - node0;
-    if (node0 < 0 || T < 0 || T > cap) T = 0;
+    const int64_t total = a.tree_indptr[a.batch];
+    if (node0 < 0 || T < 0 || T > cap || (int64_t)node0 + T > total) {
+      T = 0;
+      return MLA_VERIFY_STATUS_TREE_RANGE;
+    }
   }
+  return 0;
 }
 
-// Returns false for a workgroup with nothing to do: past the last split group,
-// or a row block past its sequence's T_b * H rows (row blocks are counted for
-// the largest tree; smaller trees leave the rest idle).
-__device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w, int rows_per_block) {
+// Fills w for this workgroup. Returns false past the last split group (no
+// work at all). A row block past its sequence's T_b * H rows (row blocks are
+// counted for the largest tree) is still mapped; the caller checks w.rows.
+__device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w) {
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int local = bid / kXcds;
@@ -169,9 +190,8 @@ __device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w, int
     else hi = mid - 1;
   }
   w.b = lo;
-  seq_tree(a, w.b, w.node0, w.T);
+  w.tree_status = seq_tree(a, w.b, w.node0, w.T);
   w.rows = w.T * a.heads;
-  if (w.rb * rows_per_block >= w.rows) return false;
   w.S = a.split_offset[w.b + 1] - a.split_offset[w.b];
   w.s = (cg - a.group_offset[w.b]) * a.group;
   w.s_last = min(w.s + a.group, w.S);
@@ -184,6 +204,39 @@ __device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w, int
   w.tile_begin = split_tile(w.s, w.ntiles, w.S);
   w.tile_end = split_tile(w.s_last, w.ntiles, w.S);
   return true;
+}
+
+// The per-sequence status words of the run (one int32 per sequence, written
+// by every run): the workgroup of a sequence's first split group and first row
+// block writes its word, and also the words of the neighbouring sequences that
+// have no workgroup at all (planned with an empty tree), up to the previous
+// sequence with one and, for the last such sequence, to the end of the batch.
+// Bits: MLA_VERIFY_STATUS_BAD_PARENT when some node's parent is not in
+// -1..node-1 (the rows of every node whose ancestor chain meets it are NaN);
+// MLA_VERIFY_STATUS_SHORT_KV when N_b < T_b (every row is NaN);
+// MLA_VERIFY_STATUS_TREE_RANGE when the device tree entries are out of range
+// (no row of the sequence is written). Every thread of the workgroup calls it.
+template <int kThreadsN>
+__device__ void write_status(const VerifyArgs& a, const BlockWork& w) {
+  if (!(w.rb == 0 && w.s == 0)) return;  // uniform over the workgroup
+  int bad = 0;
+  for (int t = threadIdx.x; t < w.T; t += kThreadsN) {
+    const int p = a.parents[w.node0 + t];
+    bad |= (p < -1 || p >= t) ? 1 : 0;
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x != 0) return;
+  a.status[w.b] = w.tree_status | (bad ? MLA_VERIFY_STATUS_BAD_PARENT : 0) |
+                  (w.P < 0 ? MLA_VERIFY_STATUS_SHORT_KV : 0);
+  // Sequences without a split group hold no tree node in the plan; with
+  // device tree offsets, one that claims nodes is out of range.
+  auto empty_status = [&](int b2) {
+    int n0, t2;
+    return seq_tree(a, b2, n0, t2);
+  };
+  for (int b2 = w.b - 1; b2 >= 0 && a.split_offset[b2 + 1] == a.split_offset[b2]; --b2) a.status[b2] = empty_status(b2);
+  if (a.split_offset[w.b + 1] == a.split_offset[a.batch])
+    for (int b2 = w.b + 1; b2 < a.batch; ++b2) a.status[b2] = empty_status(b2);
 }
 
 // Masks and scales the 16 scores this lane holds in an S^T block and returns
@@ -214,39 +267,81 @@ namespace bf16k {
 constexpr int kThreads = 256;
 constexpr int kRows = 128;
 constexpr int kNbuf = 3;                        // LDS ring of key tiles
-// Padded kv_c row: 1168 B = 292 dwords = 36 (mod 64 banks). The 16 keys one
-// QK operand read serves per LDS cycle then start in 16 distinct 4-bank
-// groups (conflict-free); the transpose reads of PV see 2-way conflicts,
-// which no plain padding avoids together with the former.
-constexpr int kCRow = kDl * 2 + 144;
-constexpr int kCBytes = kKeysPerTile * kCRow;   // kv_c part of a tile
+// The kv_c part of a tile: wave w's 8 keys (8w..8w+7) fill region w, eight
+// 1 KB blocks and a 128 B pad. Block j holds 16-byte chunks 8j..8j+7
+// (features 64j..64j+63) of the 8 keys, ordered [chunk c % 8][key slot], and
+// key r sits in slot r ^ 4 when (c % 8) / 2 is odd. Every load of a tile
+// then takes its address per lane (lane i: chunk i/8 of key slot i%8, no
+// row address to broadcast), and both read patterns are conflict-free: a QK
+// operand read (16 keys, one chunk) covers 2 x 128 contiguous bytes in two
+// regions 128 bytes apart (mod 256), and a PV transpose read (4 keys x 16
+// features per 16 lanes) puts the two 16-lane groups of a half-wave on
+// disjoint banks through the key-slot swizzle.
+constexpr int kRegion = 8 * 1024 + 128;
+constexpr int kCBytes = 4 * kRegion;           // kv_c part of a tile
 constexpr int kPeRow = kDr * 2;                 // 128 B, 16-byte chunks XOR-swizzled by key
-constexpr int kBufBytes = kCBytes + kKeysPerTile * kPeRow;  // 41472
-constexpr int kPBytes = kRows * kKeysPerTile * 2;           // 8192 per tile, double-buffered
-// Page-table entries travel global -> LDS too, into a ring of kIdxRing tiles,
-// kIdxLead tiles before the keys they name are fetched; the addresses of a
-// tile's loads are prepared one iteration before the loads are issued.
-constexpr int kIdxRing = 4;
-constexpr int kIdxLead = 3;
-constexpr int kIdxBytes = kIdxRing * kKeysPerTile * 4;      // 512
+constexpr int kBufBytes = kCBytes + kKeysPerTile * kPeRow;  // 37376
+__host__ __device__ constexpr int kvc_swizzle(int chunk_in_block) { return ((chunk_in_block >> 1) & 1) << 2; }
+// Page-table entries travel global -> LDS too, in batches of kIdxBatch tiles
+// (tiles 8B..8B+7, one 64-lane load per wave: its 8 keys of each tile) into
+// a per-wave ring of two batches; batch B goes out in the iteration of tile
+// 8B - kIdxLead, at least one iteration before the addresses of its first
+// tile's loads are prepared (tile t+3 in iteration t).
+constexpr int kIdxBatch = 8;
+constexpr int kIdxLead = 4;
+constexpr int kIdxWaveBytes = 2 * kIdxBatch * 8 * 4;          // 512 per wave
+constexpr int kIdxBytes = 4 * kIdxWaveBytes;                  // 2048
 constexpr int kAncBytes = kRows * kMaskWords * 8;             // ancestor mask words of each row
 // The rope part of Q (64 features of each row) as each lane's four MFMA
 // operand fragments, [wave][fragment][lane] x 16 bytes.
 constexpr int kQpeBytes = kRows * kDr * 2;                     // 16384
-constexpr int kSmem = kNbuf * kBufBytes + 2 * kPBytes + kIdxBytes + kAncBytes + kQpeBytes;
+constexpr int kSmem = kNbuf * kBufBytes + kIdxBytes + kAncBytes + kQpeBytes;
 // Vector-memory stores one wave issues for a split partial: (m, l) plus
-// 4 row blocks x 4 feature blocks x 2 16-byte pieces. The wait after a split
-// boundary lets this many operations stay outstanding; it is safe as long as
-// the compiler emits at least this many store instructions, which holds
-// because no two of these stores are adjacent in memory (none can merge) and
-// none is wider than the widest store instruction.
-constexpr int kPartialStores = 1 + 4 * 4 * 2;
-// Vector-memory instructions each wave issues per tile: 8 kv_c rows, one
-// block of 8 k_pe rows, one block of 8 page-table entries.
-constexpr int kVmemPerTile = 10;
+// 16 feature blocks x 2 16-byte pieces. The wait after a split boundary lets
+// this many operations stay outstanding; it is safe as long as the compiler
+// emits at least this many store instructions, which holds because no two of
+// these stores are adjacent in memory (none can merge) and none is wider than
+// the widest store instruction.
+constexpr int kPartialStores = 1 + 16 * 2;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
-// Trees above 64 nodes build their masks in the P buffers before first use.
-static_assert(kTreeScratchBytes <= 2 * kPBytes, "tree mask scratch");
+// Trees above 64 nodes build their masks in the ring buffer of the third
+// tile, which is first loaded after the pipeline's first barrier.
+static_assert(kTreeScratchBytes <= kBufBytes, "tree mask scratch");
+
+// MFMA order of one pipeline iteration (tile t in LDS for PV, tile t+1 for
+// QK): the first kPvHead PV MFMAs of tile t, whose operands are read before
+// the barrier, cover the latency of the first key reads of tile t+1; then the
+// 36 QK MFMAs of tile t+1 (4 rope, 32 latent chunks); then the other 28 PV
+// MFMAs, which the softmax of tile t+1 runs beside. PV MFMA (u, fb): key step u
+// (16 keys) of output feature block fb (32 features).
+constexpr int kPvHead = 4;
+constexpr int kQkOps = 36;
+constexpr int kOps = kQkOps + 32;
+// Operand reads are issued kAhead MFMAs before their MFMA (a ring of
+// kAhead + 1 fragments).
+constexpr int kAhead = 4;
+constexpr int kRing = kAhead + 1;
+static_assert(kAhead <= kPvHead, "the reads issued before the barrier must be of tile t");
+struct Op {
+  bool pv;
+  int u, fb;  // PV: key step, feature block
+  int c;      // QK: 0..3 rope chunks, 4..35 latent chunks 0..31
+};
+__host__ __device__ constexpr Op iter_op(int j) {
+  return j < kPvHead ? Op{true, 0, j, 0}
+                     : j < kPvHead + kQkOps ? Op{false, 0, 0, j - kPvHead}
+                                             : Op{true, (j - kQkOps) >> 4, (j - kQkOps) & 15, 0};
+}
+// Slots (MFMA indices) of the other work of an iteration: the loads of tile
+// t+2 (one part every third QK MFMA, the page-table block with the first),
+// the softmax of tile t+1 (after its last QK MFMA has left the pipe), and the
+// address preparation of tile t+3's loads.
+constexpr int kDmaSlot0 = kPvHead + 2, kDmaStride = 3;
+constexpr int kSoftmaxSlot0 = kPvHead + kQkOps;
+constexpr int kSoftmaxSteps = 28;
+constexpr int kPrepSlots[3] = {kPvHead + kQkOps + 1, kPvHead + kQkOps + 12, kPvHead + kQkOps + 22};
+static_assert(kDmaSlot0 + kDmaStride * 8 < kPvHead + kQkOps, "loads go out during QK");
+static_assert(kSoftmaxSlot0 + kSoftmaxSteps <= kOps, "softmax fits the PV MFMAs");
 }  // namespace bf16k
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -259,151 +354,90 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // waits for them explicitly with wait_vmem<>. Vector-memory loads retire in
 // order, so the compiler's waits for its own loads stay correct.
 
-// Lanes 0..7 fetch the page-table entries of this wave's 8 keys of `tile`
-// into ring slot tile % kIdxRing (one global_load_lds_dword; tile >= 0 and
-// kIdxRing is a power of two). Positions past
-// `jmax` (the split's last key) are clamped to it: those keys are loaded but
-// either masked out of the softmax (past the sequence) or never computed
-// (past the split), and their data is a real, finite token.
-__device__ __forceinline__ void issue_tile_index(const VerifyArgs& a, char* idx_ring, int kv0, int jmax,
-                                                 int tile) {
+// The page-table entries of this wave's 8 keys of tiles 8B..8B+7 (batch B >=
+// 0), lane i fetching key i%8 of tile 8B + i/8 into ring half B % 2 (one
+// 64-lane global_load_lds_dword, no divergence). Positions past `jmax` (the
+// group's last key) are clamped to it: those keys are loaded but either
+// masked out of the softmax (past the sequence) or never computed (past the
+// group), and their data is a real, finite token.
+__device__ __forceinline__ void issue_index_batch(const VerifyArgs& a, char* idx_ring, int kv0, int jmax, int batch) {
   using namespace bf16k;
   const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
-  if (lane < 8) {
-    const int j = min(tile * kKeysPerTile + wave * 8 + lane, jmax);
-    const uint32_t m0 =
-        __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + ((tile & (kIdxRing - 1)) * kKeysPerTile + wave * 8) * 4));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0),
-                 "v"((uint64_t)(a.kv_indices + kv0 + j))
-                 : "memory", "m0");
-  }
+  const int j = min((batch * kIdxBatch + (lane >> 3)) * kKeysPerTile + wave * 8 + (lane & 7), jmax);
+  const uint32_t m0 = lds_addr(idx_ring) + wave * kIdxWaveBytes + (batch & 1) * (kIdxWaveBytes / 2);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0),
+               "v"((uint64_t)(a.kv_indices + kv0 + j))
+               : "memory", "m0");
 }
 
-// Slots of this wave's 8 keys of `tile` (lane & 7 -> key), read back from the
-// index ring once this wave's load of them has completed.
-__device__ __forceinline__ int tile_slots(const char* idx_ring, int tile) {
+// Key slot (0..7 within this wave's 8 keys) whose kv_c this lane loads:
+// chunk lane/8 of the key in slot lane%8, un-swizzled.
+__device__ __forceinline__ int lane_kvc_key() {
+  const int lane = lane_id();
+  return (lane & 7) ^ bf16k::kvc_swizzle(lane >> 3);
+}
+// Page-table entry of key `key` (0..7) of this wave's share of `tile`, read
+// back from the index ring once this wave's load of it has completed.
+__device__ __forceinline__ int tile_slot(const char* idx_ring, int tile, int key) {
   using namespace bf16k;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;
-  return *(const int*)(idx_ring + ((tile & (kIdxRing - 1)) * kKeysPerTile + wave * 8 + (lane_id() & 7)) * 4);
+  return *(const int*)(idx_ring + wave * kIdxWaveBytes + ((tile & (2 * kIdxBatch - 1)) * 8 + key) * 4);
 }
 
 // Loads of this wave's share of one tile (keys 8w..8w+7) into an LDS buffer,
-// with every address prepared once so that each load is a couple of
-// instructions: the 64-bit kv_c row addresses sit in lanes 0..7, the k_pe
-// address is per lane. Parts 0..7 are the kv_c rows (1 KB, one 64-lane
-// 16-byte load from a scalar row address each); part 8 is the eight 128-byte
-// k_pe rows together, lane i fetching chunk (i%8) ^ (i/8) so that the chunks of
-// one key land XOR-swizzled by the key index.
+// every address prepared once per tile and held per lane. Parts 0..7 are the
+// kv_c blocks: part j copies chunks 8j..8j+7 of the 8 keys (lane i: chunk
+// 8j + i/8 of the key in slot i%8) with one 64-lane 16-byte load whose
+// immediate offset, 128j, moves the global and the LDS address alike. Part 8
+// is the eight 128-byte k_pe rows together, lane i fetching chunk
+// (i%8) ^ (i/8) so that the chunks of one key land XOR-swizzled by the key.
 constexpr int kTileParts = 9;
 struct TileLoads {
-  uint32_t row_lo, row_hi;  // lanes 0..7: kv_c row address of key 8w + lane
-  uint64_t kpe;             // per lane: k_pe chunk address
-  uint32_t lds_base;        // wave-uniform: LDS address of this wave's first row
+  uint64_t kvc;       // per lane: global address of its kv_c chunk in block 0
+  uint64_t kpe;       // per lane: k_pe chunk address
+  uint32_t lds_base;  // wave-uniform: LDS address of this wave's region
 };
 
-// prepare_tile in three steps (so a loop can spread them between MFMAs):
-// kv_c row addresses, then the lane shuffle for k_pe, then the k_pe address.
-// buf_lds: LDS address of the destination buffer.
-__device__ __forceinline__ void prepare_rows(TileLoads& t, const VerifyArgs& a, uint32_t buf_lds, int slots, int wave) {
+// prepare_tile in two steps (so a loop can spread them between MFMAs).
+// buf_lds: LDS address of the destination buffer; kslot: page-table entry
+// of lane_kvc_key(); pslot: that of key lane/8.
+__device__ __forceinline__ void prepare_rows(TileLoads& t, const VerifyArgs& a, uint32_t buf_lds, int kslot, int wave) {
   using namespace bf16k;
-  const uint64_t row = (uint64_t)(uintptr_t)a.kv_c + (uint64_t)(int64_t)slots * (uint64_t)a.kv_c_stride * 2u;
-  t.row_lo = (uint32_t)row;
-  t.row_hi = (uint32_t)(row >> 32);
-  t.lds_base = buf_lds + wave * 8 * kCRow;
+  t.kvc = (uint64_t)(uintptr_t)a.kv_c + (uint64_t)(int64_t)kslot * (uint64_t)a.kv_c_stride * 2u +
+          (uint32_t)(lane_id() >> 3) * 16u;
+  t.lds_base = buf_lds + wave * kRegion;
 }
-__device__ __forceinline__ int prepare_kpe_slot(int slots) { return shfl_i32(slots, lane_id() >> 3); }
-__device__ __forceinline__ void prepare_kpe(TileLoads& t, const VerifyArgs& a, int kslot) {
+__device__ __forceinline__ void prepare_kpe(TileLoads& t, const VerifyArgs& a, int pslot) {
   const int lane = lane_id();
   const int chunk = (lane & 7) ^ (lane >> 3);
-  t.kpe = (uint64_t)(uintptr_t)a.k_pe + ((uint64_t)(int64_t)kslot * (uint64_t)a.k_pe_stride + chunk * 8) * 2u;
+  t.kpe = (uint64_t)(uintptr_t)a.k_pe + ((uint64_t)(int64_t)pslot * (uint64_t)a.k_pe_stride + chunk * 8) * 2u;
 }
-__device__ __forceinline__ TileLoads prepare_tile(const VerifyArgs& a, const char* buf, int slots, int wave) {
+__device__ __forceinline__ TileLoads prepare_tile(const VerifyArgs& a, const char* buf, const char* idx_ring, int tile,
+                                                  int wave) {
   TileLoads t;
-  prepare_rows(t, a, lds_addr(buf), slots, wave);
-  prepare_kpe(t, a, prepare_kpe_slot(slots));
+  prepare_rows(t, a, lds_addr(buf), tile_slot(idx_ring, tile, lane_kvc_key()), wave);
+  prepare_kpe(t, a, tile_slot(idx_ring, tile, lane_id() >> 3));
   return t;
 }
 
-__device__ __forceinline__ void issue_tile_part(const TileLoads& t, int wave, int part) {
+template <int kPart>
+__device__ __forceinline__ void issue_tile_part(const TileLoads& t, int wave) {
   using namespace bf16k;
-  if (part < 8) {
-    // readlane returns int: widen through uint32_t so the low word is not sign-extended.
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)t.row_lo, part);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)t.row_hi, part);
-    const uint64_t row = ((uint64_t)hi << 32) | (uint64_t)lo;
-    const uint32_t m0 = t.lds_base + part * kCRow;
-    // s_nop 4: the scalar base was just written by v_readlane, and a VMEM read
-    // of a VALU-written SGPR needs 5 wait states; it also covers the one wait
-    // state between writing M0 and an LDS-DMA load.
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0),
-                 "v"((uint32_t)lane_id() * 16), "s"(row)
+  if constexpr (kPart < 8) {
+    // LDS destination M0 + 128*kPart + 16*lane = block kPart of the region.
+    const uint32_t m0 = t.lds_base + (1024 - 128) * kPart;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%2" ::"s"(m0), "v"(t.kvc),
+                 "i"(128 * kPart)
                  : "memory", "m0");
   } else {
-    const uint32_t m0 = t.lds_base - wave * 8 * kCRow + kCBytes + wave * 8 * kPeRow;
+    const uint32_t m0 = t.lds_base - wave * kRegion + kCBytes + wave * 8 * kPeRow;
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(t.kpe)
                  : "memory", "m0");
   }
 }
 
 __device__ __forceinline__ void issue_tile(const TileLoads& t, int wave) {
-#pragma unroll
-  for (int part = 0; part < kTileParts; ++part) issue_tile_part(t, wave, part);
-}
-
-// S^T[32 keys x 32 rows] = K . Q^T for this wave's rows from LDS tile `buf`:
-// 9 batches of 4 MFMAs over the 576 features. Batch kQkRopeBatch is the rope
-// part, with both operands from LDS (Q's rope fragments live there, at `qpe`
-// for this lane, to spare 16 registers); the others take the latent part of Q
-// from registers. First is best (measured: the middle costs 1.5%, the end
-// 18%, where its extra operand registers meet the PV prefetch). Each batch's
-// LDS reads are issued during the previous batch; the scheduling barriers
-// stop the compiler from hoisting every read at once. between(kb) runs after
-// the MFMAs of batch kb.
-constexpr int kQkRopeBatch = 0;
-// With kQpePreloaded the caller has already read the rope part of Q into
-// qf_pre (the tile loop reads it across its barrier); otherwise qf_pre is
-// unused and it is read here.
-template <bool kQpePreloaded, typename Between>
-__device__ __forceinline__ f32x16_t qk_tile(const char* buf, const bf16x8_t (&qreg)[32], const char* qpe, int k_off,
-                                            int kpe_off, int kpe_sw, int half, const bf16x8_t (&qf_pre)[4],
-                                            Between&& between) {
-  f32x16_t sacc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-  bf16x8_t kf[2][4], qf[4];
-  if constexpr (kQpePreloaded) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qf[j] = qf_pre[j];
-  }
-  auto load_batch = [&](int b, bf16x8_t (&dst)[4]) {
-    if (b == kQkRopeBatch) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dst[j] = *(const bf16x8_t*)(buf + kpe_off + (((2 * j + half) ^ kpe_sw) << 4));
-        if constexpr (!kQpePreloaded) qf[j] = *(const bf16x8_t*)(qpe + j * 64 * 16);
-      }
-    } else {
-      const int c0 = 4 * (b < kQkRopeBatch ? b : b - 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = *(const bf16x8_t*)(buf + k_off + (c0 + j) * 32);
-    }
-  };
-  load_batch(0, kf[0]);
-#pragma unroll
-  for (int kb = 0; kb < 9; ++kb) {
-    if (kb + 1 < 9) load_batch(kb + 1, kf[(kb + 1) & 1]);
-    // Keep the reads of batch kb+1 ahead of the MFMAs of batch kb (left to
-    // itself the scheduler sinks them below and reuses the registers).
-    __builtin_amdgcn_sched_barrier(0);
-    const int c0 = 4 * (kb < kQkRopeBatch ? kb : kb - 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb & 1][j], kb == kQkRopeBatch ? qf[j] : qreg[c0 + j], sacc, 0,
-                                                     0, 0);
-    between(kb);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  return sacc;
+  static_for<kTileParts>([&](auto part) { issue_tile_part<decltype(part)::value>(t, wave); });
 }
 
 // Values 4*gi .. 4*gi+3 of an accumulator block, read out of the
@@ -425,33 +459,49 @@ __device__ __forceinline__ f32x4_t read_acc4(const f32x16_t& acc, int gi) {
 // 20 wait states: more than any 32x32 MFMA result needs before it is read.
 __device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 15\n\ts_nop 3" ::: "memory"); }
 
+// QK MFMAs with the S^T accumulator in VGPRs. Left to itself the compiler
+// gives every MFMA accumulator an AGPR block; all 256 hold O, so it would park
+// an output block in VGPRs around every QK and copy the scores out after it.
+// The compiler does not see these as MFMAs: the reader of the result waits
+// with qk_result_wait() (after which the scores are ordinary VGPR values), and
+// the accumulation chain keeps the same registers (srcC = vdst), which needs
+// no wait states between its MFMAs.
+__device__ __forceinline__ void mfma_qk_first(f32x16_t& acc, const bf16x8_t& k, const bf16x8_t& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void mfma_qk(f32x16_t& acc, const bf16x8_t& k, const bf16x8_t& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void qk_result_wait(f32x16_t& acc) { asm volatile("s_nop 15\n\ts_nop 3" : "+v"(acc)); }
+
 __global__ void __launch_bounds__(bf16k::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   using namespace bf16k;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
-  char* const pbuf0 = smem + kNbuf * kBufBytes;
-  char* const idx_ring = pbuf0 + 2 * kPBytes;
+  char* const idx_ring = smem + kNbuf * kBufBytes;
   uint64_t* const anc_lds = (uint64_t*)(idx_ring + kIdxBytes);
   char* const qpe_lds = idx_ring + kIdxBytes + kAncBytes;
 
   BlockWork w;
-  if (!map_block(a, w, kRows)) return;
+  if (!map_block(a, w)) return;
+  write_status<kThreads>(a, w);
+  if (w.rb * kRows >= w.rows) return;
   const int H = a.heads;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;  // uniform: keep it scalar
   const int half = lane >> 5;   // k slice of MFMA operands / key quartet of S^T rows
-  const int qcol = lane & 31;   // column of the 32x32 blocks
+  const int qcol = lane & 31;   // column of the 32x32 blocks: this lane's query row
 
-  // The page-table entries of the first three tiles go out first, so that
-  // their round trip overlaps the loads of Q and of the tree.
+  // The page-table entries of the first two batches of tiles go out first,
+  // so that their round trip overlaps the loads of Q and of the tree.
   const int jmax0 = min(w.N, w.tile_end * kKeysPerTile) - 1;
   if (w.tile_begin < w.tile_end) {
-#pragma unroll
-    for (int t = 0; t < 3; ++t) issue_tile_index(a, idx_ring, w.kv0, jmax0, w.tile_begin + t);
+    issue_index_batch(a, idx_ring, w.kv0, jmax0, w.tile_begin / kIdxBatch);
+    issue_index_batch(a, idx_ring, w.kv0, jmax0, w.tile_begin / kIdxBatch + 1);
   }
 
-  // ---- QK role: this lane's query row (wave owns rows 32w..32w+31) ---------
+  // ---- this lane's query row: wave w owns rows 32w..32w+31 of the block ----
   const int r_local = w.rb * kRows + wave * 32 + qcol;
   const int r_eff = min(r_local, w.rows - 1);
   const int64_t grow = (int64_t)w.node0 * H + r_eff;
@@ -468,10 +518,10 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   }
   // This lane's ancestor mask waits in LDS (read by the few tiles that reach
   // the tree tail and by the epilogue) instead of holding registers through
-  // the tile loop. Only the QK owner (half 0) writes it; the first barrier of
-  // the pipeline orders the write before every read. Trees of up to 64 nodes
-  // take the one-wave builder; larger ones are built by the workgroup in the
-  // P buffers, which are first written after that barrier.
+  // the tile loop. Only half 0 writes it; the first barrier of the pipeline
+  // orders the write before every read. Trees of up to 64 nodes take the
+  // one-wave builder; larger ones are built by the workgroup in the ring
+  // buffer of the third tile, first loaded after that barrier.
   {
     uint64_t* const dst = anc_lds + (wave * 32 + qcol) * kMaskWords;
     if (w.T <= 64) {
@@ -483,8 +533,9 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         for (int k = 1; k < kMaskWords; ++k) dst[k] = 0ull;
       }
     } else {
-      block_tree_masks<kThreads>(a.parents + w.node0, w.T, pbuf0);
-      const uint64_t* src = tree_scratch_masks(pbuf0) + (r_eff / H) * kMaskWords;
+      char* const scratch = smem + ((w.tile_begin + 2) % kNbuf) * kBufBytes;
+      block_tree_masks<kThreads>(a.parents + w.node0, w.T, scratch);
+      const uint64_t* src = tree_scratch_masks(scratch) + (r_eff / H) * kMaskWords;
       if (half == 0) {
 #pragma unroll
         for (int k = 0; k < kMaskWords; ++k) dst[k] = w.seq_ok ? src[k] : 0ull;
@@ -511,21 +562,29 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   };
 
   // Per-lane LDS address pieces.
-  // K (A operand of QK): key = qcol, 8 features at 16*kc + 8*half.
-  const int k_off = qcol * kCRow + half * 16;
+  // K (A operand of QK): key = qcol, chunk 2*kc + half (8 features at
+  // 16*kc + 8*half): region qcol/8, block kc/4, chunk slot 2*(kc%4) + half,
+  // key slot qcol%8 swizzled when kc is odd (k_off[kc % 2]).
+  const int k_reg = (qcol >> 3) * kRegion + half * 128;
+  const int k_off0 = k_reg + 16 * (qcol & 7), k_off1 = k_reg + 16 * ((qcol & 7) ^ 4);
   const int kpe_off = kCBytes + qcol * kPeRow;
   const int kpe_sw = qcol & 7;
   // V^T (A operand of PV) via transpose reads: 16-lane group g reads 4 keys x
   // 16 features; lane i of the group points at key 4*half + i/4, features
-  // 16*(g%2) + 4*(i%4) of this wave's feature range.
+  // 16*(g%2) + 4*(i%4) of the feature block. Lane l then holds feature l%32
+  // of the block for keys 4*half + 0..3 (+8 for the second read). Feature
+  // block fb of those keys: chunk 4*fb + 2*(g%2) + (i%4)/2, at byte 8*(i%2) of
+  // it, in the region of the keys' wave (plus 512*fb).
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int v_off = (4 * half + (i16 >> 2)) * kCRow + (16 * (g16 & 1) + 4 * (i16 & 3)) * 2 + wave * 4 * 64;
+  const int v_off = 256 * (g16 & 1) + 128 * ((i16 & 3) >> 1) +
+                    16 * ((4 * half + (i16 >> 2)) ^ kvc_swizzle(2 * (g16 & 1))) + 8 * (i16 & 1);
 
   // Softmax state of this lane's row (same rules as the fp32 kernel):
   // m_ref = reference max (log2 units, scaled) fixed at the first tile where
   // the row sees a key; weights are 2^(s - m_ref); if some score exceeds it by
   // more than kOverflowSlack the block repeats the split with the exact max.
-  f32x16_t oacc[16];  // [f4 * 4 + rb]: feature block 4*wave + f4, row block rb
+  // O^T of this wave's 32 rows: oacc[fb] holds features 32fb..32fb+31.
+  f32x16_t oacc[16];
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
   // Split boundaries inside the group: the weight sum of a tile that starts
   // the next split stays out of l_run (it is still in sm.psum when the split
@@ -533,77 +592,83 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   bool next_starts_split = false;
   const int s_first = w.s, c_first = w.c;
 
-  // Invisible keys of one S^T block get -inf (only tiles that reach the tree
-  // tail or the end of the sequence need this; register i holds key
-  // k0 + (i/4)*8 + 4*half + i%4).
-  auto mask_tile = [&](f32x16_t& sacc, int k0) {
+  // Invisible keys of one S^T block get -inf (register i holds key
+  // k0 + (i/4)*8 + 4*half + i%4): keys from jend on, and tail keys (from P
+  // on) outside the row's ancestor mask.
+  auto mask_tile = [&](f32x16_t& sacc, int k0, int jend) {
     const uint32_t hwin = row_window(k0 - w.P) >> (4 * half);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
       const bool tail_bit = ((hwin >> ((i >> 2) * 8 + (i & 3))) & 1u) != 0;
-      const bool vis = (j < w.P) | ((j < w.N) & tail_bit);
+      const bool vis = (j < jend) & ((j < w.P) | tail_bit);
       sacc[i] = vis ? sacc[i] : -INFINITY;
     }
   };
   // Weights of one (masked) tile for this lane's row, 2^(scale*s*log2e -
-  // m_ref), written as bf16 P^T fragments to P buffer `pb` for every wave.
-  // Split into steps 0..27 so the PV loop can interleave them with its MFMAs;
-  // step k only uses results of earlier steps. The max is taken on raw scores
-  // (scale > 0 keeps the order).
+  // m_ref), as the two bf16 P^T fragments of the PV MFMAs (key steps 0 and
+  // 1). Register i of the S^T block is key (i/4)*8 + 4*half + i%4, so
+  // fragment u (values 8u..8u+7) covers keys 16u..16u+15, in the order the
+  // V^T reads follow. Split into steps 0..kSoftmaxSteps-1 that the loop runs
+  // one per MFMA. With one wave per SIMD a VALU instruction that waits for
+  // the one before it stalls the whole instruction stream, MFMAs included,
+  // so every step only consumes results of earlier steps: the max is a tree
+  // spread over steps 0..5, and the weights are a three-stage pipeline
+  // (scale, exp2, sum) with value i in stage 1 at step 8+i. The max is taken
+  // on raw scores (scale > 0 keeps the order).
   struct SoftmaxState {
-    float m[6], mloc, mswap, nmu, psum, p[16];
-    bf16x8_t pk[2];
+    float t[7], mswap, mx, nmu, psum;
   } sm;
-  auto softmax_step = [&](int k, const f32x16_t& sc, char* pb, bool& overflow) {
-    if (k == 0) {
-      sm.m[0] = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-      sm.m[1] = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
-    } else if (k == 1) {
-      sm.m[2] = fmaxf(fmaxf(sc[6], sc[7]), sc[8]);
-      sm.m[3] = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
-    } else if (k == 2) {
-      sm.m[4] = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
-      sm.mloc = fmaxf(fmaxf(fmaxf(sm.m[0], sm.m[1]), sm.m[2]), fmaxf(fmaxf(sm.m[3], sm.m[4]), sc[15]));
-    } else if (k == 3) {
-      sm.mswap = swap_halves(sm.mloc);
-    } else if (k == 4) {
-      const float mx = fmaxf(sm.mloc, sm.mswap) * a.scale_log2;  // row max of the tile, log2 units
-      m_max = fmaxf(m_max, mx);
-      if (m_ref == -INFINITY) m_ref = mx;
-      overflow |= mx > m_ref + kOverflowSlack;
+  auto softmax_step = [&](auto kc, f32x16_t& sc, bf16x8_t (&pw)[2], bool& overflow) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k == 0) {
+      sm.t[0] = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+      sm.t[1] = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
+      sm.t[2] = fmaxf(fmaxf(sc[6], sc[7]), sc[8]);
+    } else if constexpr (k == 1) {
+      sm.t[3] = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
+      sm.t[4] = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
+      sm.t[5] = fmaxf(fmaxf(sm.t[0], sm.t[1]), sc[15]);
+    } else if constexpr (k == 2) {
+      sm.t[6] = fmaxf(fmaxf(sm.t[2], sm.t[3]), sm.t[4]);
+    } else if constexpr (k == 3) {
+      sm.t[0] = fmaxf(sm.t[5], sm.t[6]);
+    } else if constexpr (k == 4) {
+      sm.mswap = swap_halves(sm.t[0]);
+    } else if constexpr (k == 5) {
+      sm.mx = fmaxf(sm.t[0], sm.mswap) * a.scale_log2;
+    } else if constexpr (k == 6) {
+      m_max = fmaxf(m_max, sm.mx);
+      if (m_ref == -INFINITY) m_ref = sm.mx;
+    } else if constexpr (k == 7) {
+      overflow |= sm.mx > m_ref + kOverflowSlack;
       sm.nmu = m_ref == -INFINITY ? 0.f : -m_ref;
       sm.psum = 0.f;
-    } else if (k >= 5 && k < 21) {
-      const int i = k - 5;
-      sm.p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], a.scale_log2, sm.nmu));
-      sm.psum += sm.p[i];
-    } else if (k == 21 || k == 22) {
-      const int u = k - 21;
+    } else if constexpr (k >= 8 && k < 8 + 18) {
+      constexpr int i = k - 8;
+      if constexpr (i < 16) sc[i] = __builtin_fmaf(sc[i], a.scale_log2, sm.nmu);
+      if constexpr (i >= 1 && i <= 16) sc[i - 1] = __builtin_amdgcn_exp2f(sc[i - 1]);
+      if constexpr (i >= 2) sm.psum += sc[i - 2];
+      if constexpr (i == 10 || i == 17) {
+        constexpr int u = i == 10 ? 0 : 1;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sm.pk[u][jj] = (__bf16)sm.p[8 * u + jj];
-    } else if (k == 23 || k == 24) {
-      const int u = k - 23;
-      *(bf16x8_t*)(pb + ((wave * 2 + u) * 64 + lane) * 16) = sm.pk[u];
-    } else if (k == 25) {
+        for (int jj = 0; jj < 8; ++jj) pw[u][jj] = (__bf16)sc[8 * u + jj];
+      }
+    } else if constexpr (k == 26) {
       if (!next_starts_split) l_run += sm.psum;
     }
   };
-  constexpr int kSoftmaxSteps = 26;
-  constexpr int kSoftmaxLag = 3;  // PV MFMAs issued before the first softmax step
-  auto softmax_to_lds = [&](const f32x16_t& sc, char* pb, bool& overflow) {
-#pragma unroll
-    for (int k = 0; k < kSoftmaxSteps; ++k) softmax_step(k, sc, pb, overflow);
-  };
+  constexpr int kStepsUsed = 27;
+  static_assert(kSoftmaxSteps >= kStepsUsed, "softmax steps");
   // A tile needs masking when it reaches the tree tail (or the sequence end).
   auto needs_mask = [&](int k0) { return k0 + kKeysPerTile > w.P; };
 
-  // Partial of global split c (sequences with several splits): (m, l) from the QK
-  // owner lanes of each row, and this wave's raw O^T blocks in bf16 (half the
-  // bytes of fp32; the rounding is relative to each partial and averages out
-  // in the merge). No exchange between waves, so no barrier.
-  // Accumulator register i of block (f4, rb) holds feature
-  // 32*(4*wave + f4) + (i/4)*8 + 4*half + i%4 of row 32*rb + qcol.
+  // Partial of global split c (sequences with several splits): (m, l) of this
+  // lane's row (both lanes of a row hold the same values) and its raw O in
+  // bf16 (half the bytes of fp32; the rounding is relative to each partial and
+  // averages out in the merge). Each wave writes only its own rows, so no
+  // exchange and no barrier. Accumulator register i of block fb holds feature
+  // 32fb + (i/4)*8 + 4*half + i%4 of the lane's row.
   //
   // The partial arrays have a.part_rows (a multiple of kRows) rows per split,
   // so the rows past T_b * H of the last row block have room and every
@@ -618,67 +683,51 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     const float l_tot = l_part + swap_halves(l_part);
     const bool node_ok = row_valid();
     mfma_result_wait();  // the last PV MFMAs may have just been issued
-    // (m, l) of the row; both lanes of a row hold the same values.
     const int64_t prow = (int64_t)c * a.part_rows + w.rb * kRows + wave * 32 + qcol;
     *(float2*)(a.part_ml + 2 * prow) = make_float2(node_ok ? m_ref : NAN, node_ok ? l_tot : NAN);
+    __bf16* dst = (__bf16*)a.part_o + prow * kDl + 8 * half;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int r = w.rb * kRows + rb * 32 + qcol;
-      __bf16* dst = (__bf16*)a.part_o + ((int64_t)c * a.part_rows + r) * kDl + 8 * half;
+    for (int fb = 0; fb < 16; ++fb)
 #pragma unroll
-      for (int f4 = 0; f4 < 4; ++f4)
+      for (int m = 0; m < 2; ++m) {
+        // Values 2m and 2m+1 (features 16m + 4*half + 0..3 and 16m + 8 +
+        // 4*half + 0..3 of the block) become 8 consecutive features per lane
+        // by one exchange between the wave halves: the lower half keeps
+        // 16m..16m+7, the upper half gets 16m+8..16m+15.
+        const f32x4_t t0 = read_acc4(oacc[fb], 2 * m);
+        const f32x4_t t1 = read_acc4(oacc[fb], 2 * m + 1);
+        uint32_t x[2], y[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          // Values 2m and 2m+1 (features 16m + 4*half + 0..3 and 16m + 8 +
-          // 4*half + 0..3) become 8 consecutive features per lane by one
-          // exchange between the wave halves: the lower half keeps 16m..16m+7,
-          // the upper half gets 16m+8..16m+15.
-          const f32x4_t t0 = read_acc4(oacc[f4 * 4 + rb], 2 * m);
-          const f32x4_t t1 = read_acc4(oacc[f4 * 4 + rb], 2 * m + 1);
-          uint32_t x[2], y[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            x[e] = pack_bf16x2(t0[2 * e], t0[2 * e + 1]);
-            y[e] = pack_bf16x2(t1[2 * e], t1[2 * e + 1]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
-            x[e] = sw[0];
-            y[e] = sw[1];
-          }
-          *(u32x4_t*)(dst + 32 * (4 * wave + f4) + 16 * m) = u32x4_t{x[0], x[1], y[0], y[1]};
-          // One pair at a time: otherwise the scheduler reads every
-          // accumulator out at once and runs out of registers.
-          __builtin_amdgcn_sched_barrier(0);
+        for (int e = 0; e < 2; ++e) {
+          x[e] = pack_bf16x2(t0[2 * e], t0[2 * e + 1]);
+          y[e] = pack_bf16x2(t1[2 * e], t1[2 * e + 1]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+          x[e] = sw[0];
+          y[e] = sw[1];
         }
-    }
+        *(u32x4_t*)(dst + 32 * fb + 16 * m) = u32x4_t{x[0], x[1], y[0], y[1]};
+        // One pair at a time: otherwise the scheduler reads every
+        // accumulator out at once and runs out of registers.
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
-  // Output of a sequence with one split: O / l and lse; each row's
-  // statistics travel from its QK owner to every wave through LDS.
+  // Output of a sequence with one split: O / l and lse of this lane's row.
   auto emit_final = [&]() {
     const float l_tot = l_run + swap_halves(l_run);
-    float2* stats = (float2*)pbuf0;  // the P buffers are free after the loop
     const bool node_ok = row_valid();
     mfma_result_wait();
-    __syncthreads();
-    if (half == 0) stats[wave * 32 + qcol] = make_float2(node_ok ? m_ref : NAN, l_tot);
-    __syncthreads();
+    if (r_local >= w.rows) return;
+    const int64_t g = (int64_t)w.node0 * H + r_local;
+    float* dst = a.out + g * kDl + 4 * half;
+    const float mul = node_ok ? 1.f / l_tot : NAN;
+    if (half == 0 && a.lse) a.lse[g] = node_ok ? (m_ref + __log2f(l_tot)) * kLn2 : NAN;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int r = w.rb * kRows + rb * 32 + qcol;
-      if (r >= w.rows) continue;
-      const float2 st = stats[rb * 32 + qcol];
-      const bool ok = !(st.x != st.x);
-      const int64_t g = (int64_t)w.node0 * H + r;
-      float* dst = a.out + g * kDl;
-      const float mul = ok ? 1.f / st.y : NAN;
-      if (wave == 0 && half == 0 && a.lse) a.lse[g] = ok ? (st.x + __log2f(st.y)) * kLn2 : NAN;
+    for (int fb = 0; fb < 16; ++fb)
 #pragma unroll
-      for (int f4 = 0; f4 < 4; ++f4)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const f32x4_t v = read_acc4(oacc[f4 * 4 + rb], gi);
-          *(f32x4_t*)(dst + 32 * (4 * wave + f4) + 8 * gi + 4 * half) = v * mul;
-        }
-    }
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4_t v = read_acc4(oacc[fb], gi);
+        *(f32x4_t*)(dst + 32 * fb + 8 * gi) = v * mul;
+      }
   };
 
   for (int pass = 0; pass < 2; ++pass) {
@@ -690,32 +739,52 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       const int tb = w.tile_begin, te = w.tile_end;
       const int jmax = min(w.N, te * kKeysPerTile) - 1;
       // Pipeline. Iteration t: tiles t and t+1 are in LDS, tile t+2 and the
-      // page-table entries of t+2+kIdxLead are fetched; QK and softmax of
-      // tile t+1 run while the PV of tile t (whose weights every wave wrote in
-      // the previous iteration) keeps the matrix cores busy. Tiles past the
-      // split repeat its last key (loaded, never computed), which keeps the
-      // number of loads per iteration constant.
+      // page-table entries of t+2+kIdxLead are fetched; the QK and softmax
+      // of tile t+1 run between the PV MFMAs of tile t, whose weights this
+      // wave computed in the previous iteration and holds in registers. The
+      // tiles past the group repeat its last key (loaded, never visible),
+      // which keeps the number of loads per iteration constant; the QK of
+      // the group's last iteration runs on such a tile and is masked out.
       if (pass > 0) {  // pass 0 issued these at the start
-        issue_tile_index(a, idx_ring, w.kv0, jmax, tb);
-        issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1);
-        issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 2);
+        issue_index_batch(a, idx_ring, w.kv0, jmax, tb / kIdxBatch);
+        issue_index_batch(a, idx_ring, w.kv0, jmax, tb / kIdxBatch + 1);
       }
       wait_vmem<0>();
-      issue_tile(prepare_tile(a, smem + (tb % kNbuf) * kBufBytes, tile_slots(idx_ring, tb), wave), wave);
-      issue_tile_index(a, idx_ring, w.kv0, jmax, tb + kIdxLead);
-      issue_tile(prepare_tile(a, smem + ((tb + 1) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + 1), wave), wave);
-      issue_tile_index(a, idx_ring, w.kv0, jmax, tb + 1 + kIdxLead);
-      // Loads of tile tb+2, issued at the top of the first iteration.
-      TileLoads pending =
-          prepare_tile(a, smem + ((tb + 2) % kNbuf) * kBufBytes, tile_slots(idx_ring, tb + 2), wave);
-      wait_vmem<kVmemPerTile + 1>();  // this wave's part of tile tb
+      issue_tile(prepare_tile(a, smem + (tb % kNbuf) * kBufBytes, idx_ring, tb, wave), wave);
+      issue_tile(prepare_tile(a, smem + ((tb + 1) % kNbuf) * kBufBytes, idx_ring, tb + 1, wave), wave);
+      // Loads of tile tb+2, issued during the first iteration.
+      TileLoads pending = prepare_tile(a, smem + ((tb + 2) % kNbuf) * kBufBytes, idx_ring, tb + 2, wave);
+      wait_vmem<kTileParts>();  // this wave's part of tile tb
       block_sync();
+      // Scores and weights of the first tile.
+      bf16x8_t pk[2];
       {
-        bf16x8_t qf_none[4];
-        f32x16_t s0 = qk_tile<false>(smem + (tb % kNbuf) * kBufBytes, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half,
-                                     qf_none, [](int) {});
-        if (needs_mask(tb * kKeysPerTile)) mask_tile(s0, tb * kKeysPerTile);
-        softmax_to_lds(s0, pbuf0 + (tb & 1) * kPBytes, overflow);
+        const char* const kb = smem + (tb % kNbuf) * kBufBytes;
+        // K fragment of QK MFMA c (0..3 rope, 4..35 latent chunks)
+        auto read_k = [&](auto cc) -> bf16x8_t {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (c < 4) return *(const bf16x8_t*)(kb + kpe_off + (((2 * c + half) ^ kpe_sw) << 4));
+          else {
+            constexpr int kc = c - 4;
+            return *(const bf16x8_t*)(kb + ((kc & 1) ? k_off1 : k_off0) + 1024 * (kc >> 2) + 256 * (kc & 3));
+          }
+        };
+        bf16x8_t qf[4], ring[kRing];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qf[j] = *(const bf16x8_t*)(qpe_lane + j * 64 * 16);
+        static_for<kAhead>([&](auto j) { ring[j % kRing] = read_k(j); });
+        f32x16_t s0;
+        static_for<kQkOps>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (c + kAhead < kQkOps) ring[(c + kAhead) % kRing] = read_k(std::integral_constant<int, c + kAhead>{});
+          if constexpr (c == 0) mfma_qk_first(s0, ring[0], qf[0]);
+          else if constexpr (c < 4) mfma_qk(s0, ring[c % kRing], qf[c]);
+          else mfma_qk(s0, ring[c % kRing], qreg[c - 4]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        qk_result_wait(s0);
+        if (needs_mask(tb * kKeysPerTile)) mask_tile(s0, tb * kKeysPerTile, w.N);
+        static_for<kSoftmaxSteps>([&](auto k) { softmax_step(k, s0, pk, overflow); });
       }
 
       // Byte offsets of the buffers of tiles t, t+1 and t+2, rotated each
@@ -738,111 +807,89 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         // still be on their way.
         if (tile == split_begin && sp != s_first) wait_vmem<kPartialStores>();
         else wait_vmem<0>();
-        wait_lds();
-        // The rope part of Q is this lane's own LDS data, written once before
-        // the loop, so its reads may cross the barrier: the batch that follows
-        // it then waits for the key reads alone (measured 0.5-1.3% faster).
-        bf16x8_t qf_pre[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qf_pre[j] = *(const bf16x8_t*)(qpe_lane + j * 64 * 16);
-        block_sync();  // P(tile) and tile+1 are visible; every wave has finished PV(tile-1)
-        // Tile+2 goes into the buffer tile-1 used; its addresses were prepared
-        // during the previous iteration. One load goes after each QK batch (a
-        // burst of all nine from every wave queues in the vector-memory path
-        // and stalls the issuing waves), the page-table block with the first.
-        const char* buf = smem + bo0;
-        const char* pb = pbuf0 + (tile & 1) * kPBytes;
-        // Does tile+1 start the next split of the group?
-        next_starts_split = tile + 1 == split_end && tile + 1 < te;
-        // PV operands: P^T fragments [u][rb] and V^T fragments of two groups.
-        // The first ones are read during the last QK batch so that the first
-        // PV MFMA does not wait for them.
-        bf16x8_t pbr[2][4];
-        i16x4_t vf[2][2];
-        auto load_v = [&](int g, i16x4_t (&dst)[2]) {
-          const char* vp = buf + v_off + (16 * (g >> 2)) * kCRow + (g & 3) * 64;
-          dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vp);
-          dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 8 * kCRow));
-        };
-        auto load_p = [&](int u) {
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) pbr[u][rb] = *(const bf16x8_t*)(pb + ((rb * 2 + u) * 64 + lane) * 16);
-        };
-        auto late_part = [&](int kb) {
-          issue_tile_part(pending, wave, kb);
-          if (kb == 0) issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
-          if (kb == 7) {
-            load_p(0);
-            load_v(0, vf[0]);
+        const char* const vbase = smem + bo0 + v_off;  // tile t (PV)
+        const char* const kbuf = smem + bo1;           // tile t+1 (QK)
+        const bool has_next = tile + 1 < te;
+        next_starts_split = tile + 1 == split_end && has_next;
+        const int k1 = (tile + 1) * kKeysPerTile;
+        // Operand of MFMA j of the iteration: a V^T fragment of tile t (two
+        // transpose reads) or a K fragment of tile t+1.
+        auto read_op = [&](auto jc) -> bf16x8_t {
+          constexpr Op o = iter_op(decltype(jc)::value);
+          if constexpr (o.pv) {
+            // keys 16u + 4*half + 0..3 in region 2u, the next 8 keys in region 2u+1
+            const char* vp = vbase + 2 * o.u * kRegion + o.fb * 512;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vp);
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + kRegion));
+            return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+          else if constexpr (o.c < 4) return *(const bf16x8_t*)(kbuf + kpe_off + (((2 * o.c + half) ^ kpe_sw) << 4));
+          else {
+            constexpr int kc = o.c - 4;
+            return *(const bf16x8_t*)(kbuf + ((kc & 1) ? k_off1 : k_off0) + 1024 * (kc >> 2) + 256 * (kc & 3));
           }
         };
-        // Scores of tile+1. On the last tile there is none: all -inf (set in
-        // the PV loop) makes the softmax steps a no-op for the row state.
-        f32x16_t snext;
-        const int k1 = (tile + 1) * kKeysPerTile;
-        const bool has_next = tile + 1 < te;
-        if (has_next) {
-          snext = qk_tile<true>(smem + bo1, qreg, qpe_lane, k_off, kpe_off, kpe_sw, half, qf_pre, late_part);
-        } else {
-          issue_tile(pending, wave);
-          issue_tile_index(a, idx_ring, w.kv0, jmax, tile + 2 + kIdxLead);
-          load_p(0);
-          load_v(0, vf[0]);
-          // snext stays unset here: it is set to -inf below (a value
-          // assigned here would make the compiler move the QK result out of
-          // the accumulation registers right after the QK, to merge the two).
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // ---- O^T[this wave's 128 features x 128 rows] += V^T . P^T (tile),
-        //      with the weights of tile+1 (VALU) threaded between the MFMAs.
-        // Group g = (u, f4) = (g/4, g%4) issues 4 MFMAs (row blocks); V^T for
-        // group g+1 and P^T for u=1 are read one group ahead.
-        // Addresses of tile+3's loads (entries landed before this iteration's
-        // wait), prepared in steps between the PV MFMAs.
+        // Before the barrier: the rope part of Q (this lane's own LDS data,
+        // written once before the loop) and the operands of the first PV
+        // MFMAs (tile t has been visible since the previous barrier).
+        bf16x8_t qf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qf[j] = *(const bf16x8_t*)(qpe_lane + j * 64 * 16);
+        bf16x8_t ring[kRing];
+        static_for<kAhead>([&](auto j) { ring[j % kRing] = read_op(j); });
+        block_sync();  // tile+1 is visible; every wave has finished with tile-1
+        f32x16_t sacc;
+        bf16x8_t pn[2];
         int pslots = 0, pkslot = 0;
-        auto prepare_step = [&](int k) {
-          if (k == 0) pslots = tile_slots(idx_ring, tile + 3);
-          else if (k == 10) {
-            prepare_rows(pending, a, lds_addr(smem) + (uint32_t)bo0, pslots, wave);
-            pkslot = prepare_kpe_slot(pslots);
-          } else if (k == 20) prepare_kpe(pending, a, pkslot);
-        };
-        {
-#pragma unroll
-          for (int g = 0; g < 8; ++g) {
-            if (g + 1 < 8) load_v(g + 1, vf[(g + 1) & 1]);
-            if (g == 2) load_p(1);
-            const bf16x8_t va = __builtin_bit_cast(
-                bf16x8_t, __builtin_shufflevector(vf[g & 1][0], vf[g & 1][1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int rb = (rr + 1) & 3;  // row block 0 last (see below)
-              const int f4 = g & 3;
-              oacc[f4 * 4 + rb] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbr[g >> 2][rb], oacc[f4 * 4 + rb], 0, 0, 0);
-              const int k = 4 * g + rr;
-              if (k == kSoftmaxLag - 1) {
-                // The scores of tile+1 leave the accumulation registers only
-                // here, behind the first PV MFMAs: read right after the last
-                // QK MFMA they would stall the wave until the matrix pipe
-                // drains. (The compiler parks the QK accumulator where an
-                // output block lives; that block's first MFMA comes after.)
-                asm volatile("" : "+v"(snext));
-                if (!has_next) {
-#pragma unroll
-                  for (int i = 0; i < 16; ++i) snext[i] = -INFINITY;
-                } else if (needs_mask(k1)) {
-                  mask_tile(snext, k1);
-                }
-              }
-              if (k >= kSoftmaxLag && k - kSoftmaxLag < kSoftmaxSteps)
-                softmax_step(k - kSoftmaxLag, snext, pbuf0 + ((tile + 1) & 1) * kPBytes, overflow);
-              prepare_step(k);
-              __builtin_amdgcn_sched_barrier(0);
+        static_for<kOps>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          if constexpr (s + kAhead < kOps)
+            ring[(s + kAhead) % kRing] = read_op(std::integral_constant<int, s + kAhead>{});
+          constexpr Op o = iter_op(s);
+          if constexpr (o.pv) {
+            oacc[o.fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[s % kRing], pk[o.u], oacc[o.fb], 0, 0, 0);
+          } else if constexpr (o.c == 0) {
+            mfma_qk_first(sacc, ring[s % kRing], qf[0]);
+          } else if constexpr (o.c < 4) {
+            mfma_qk(sacc, ring[s % kRing], qf[o.c]);
+          } else {
+            mfma_qk(sacc, ring[s % kRing], qreg[o.c - 4]);
+          }
+          // Tile t+2 goes into the buffer tile t-1 used; its addresses were
+          // prepared during the previous iteration. One load every few QK
+          // MFMAs (a burst of all of them from every wave queues in the
+          // vector-memory path and stalls the issuing waves).
+          if constexpr (s >= kDmaSlot0 && (s - kDmaSlot0) % kDmaStride == 0 &&
+                        (s - kDmaSlot0) / kDmaStride < kTileParts) {
+            constexpr int part = (s - kDmaSlot0) / kDmaStride;
+            issue_tile_part<part>(pending, wave);
+            // The next page-table batch, once its ring half is free.
+            if constexpr (part == 0) {
+              const int nb = tile + kIdxLead;
+              if ((nb & (kIdxBatch - 1)) == 0 && nb / kIdxBatch >= tb / kIdxBatch + 2)
+                issue_index_batch(a, idx_ring, w.kv0, jmax, nb / kIdxBatch);
             }
           }
-        }
+          // Scores of tile t+1: tail tiles are masked; past the group's last
+          // tile nothing is visible.
+          if constexpr (s == kSoftmaxSlot0 - 1) {
+            qk_result_wait(sacc);
+            if (!has_next || needs_mask(k1)) mask_tile(sacc, k1, has_next ? w.N : 0);
+          }
+          if constexpr (s >= kSoftmaxSlot0 && s - kSoftmaxSlot0 < kSoftmaxSteps)
+            softmax_step(std::integral_constant<int, s - kSoftmaxSlot0>{}, sacc, pn, overflow);
+          // Addresses of tile t+3's loads (entries landed before this
+          // iteration's wait).
+          if constexpr (s == kPrepSlots[0]) {
+            pslots = tile_slot(idx_ring, tile + 3, lane_kvc_key());
+            pkslot = tile_slot(idx_ring, tile + 3, lane >> 3);
+          }
+          if constexpr (s == kPrepSlots[1]) prepare_rows(pending, a, lds_addr(smem) + (uint32_t)bo0, pslots, wave);
+          if constexpr (s == kPrepSlots[2]) prepare_kpe(pending, a, pkslot);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        pk[0] = pn[0];
+        pk[1] = pn[1];
         const int bt = bo0;
         bo0 = bo1;
         bo1 = bo2;
@@ -900,7 +947,9 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
   char* const qs = smem + kTileBytes;
 
   BlockWork w;
-  if (!map_block(a, w, kRows)) return;
+  if (!map_block(a, w)) return;
+  write_status<kThreads>(a, w);
+  if (w.rb * kRows >= w.rows) return;
   const int H = a.heads;
   const int lane = lane_id();
   const int half = lane >> 5;

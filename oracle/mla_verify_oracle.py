@@ -23,11 +23,10 @@ What is computed (sources are the pages this project follows):
 * Output: softmax over the visible keys, applied to ``kv_c`` (latent-space
   output; the caller applies W_UV), plus the natural-log log-sum-exp of the
   scaled scores ("output aggregation", same page, "Output Knowledge Created").
-* Trees of any size, and a different tree size per sequence: the pages describe
-  the verify kernel as taking a set of query nodes (the draft tree's leaves and
-  internal nodes) and bound neither their number nor its equality across
-  sequences ("Ground Truth in Silicon" page, "Input Knowledge Required", item
-  3). Packed ("ragged") layout: sequence b owns tree nodes
+* Trees of any size, and a different tree size per sequence: every node of the
+  draft tree is a query of the verify step, and the pages fix neither how many
+  nodes a tree has nor that every sequence has the same number ("Ground Truth
+  in Silicon" page, "Input Knowledge Required", item 3). Packed ("ragged") layout: sequence b owns tree nodes
   tree_indptr[b] .. tree_indptr[b+1]-1; its query rows and parent entries are
   stored in that order. With equal sizes T this is the [B*T] / [B, T] layout.
 * Split-KV (flash-decode, "The Information-Gathering Pivot" page, "The Context:

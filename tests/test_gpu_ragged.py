@@ -1,8 +1,8 @@
 """GPU parity for packed trees (a tree size per sequence, empty trees included)
 and trees of 65..256 nodes (multi-word ancestor masks), against the float64
-oracle. The pages give the verify kernel a set of query nodes (the draft tree's
-leaves and internal nodes) with no bound on their number ("Ground Truth in
-Silicon" page, "Input Knowledge Required", item 3)."""
+oracle. Every node of the draft tree is a query of the verify step, and the
+pages put no limit on how many there are ("Ground Truth in Silicon" page,
+"Input Knowledge Required", item 3)."""
 import numpy as np
 import pytest
 

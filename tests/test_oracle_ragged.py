@@ -1,8 +1,8 @@
 """Pins of the oracle's packed ("ragged") trees and of trees above 64 nodes.
 
-The pages give the verify kernel a set of query nodes (the draft tree's leaves
-and internal nodes) with no bound on their number ("Ground Truth in Silicon"
-page, "Input Knowledge Required", item 3). Each test ties the oracle to
+Every node of the draft tree is a query of the verify step, and the pages put
+no limit on how many there are ("Ground Truth in Silicon" page, "Input
+Knowledge Required", item 3). Each test ties the oracle to
 something other than itself: separate single-sequence runs on hand-sliced
 inputs, the scalar brute force (its own visibility walk), torch SDPA in float64
 with a causal mask, a boolean transitive closure, and a planted dominant key.

@@ -189,6 +189,27 @@ mla_status mla_verify_run_varlen(mla_verify_plan_t plan, const void* q_nope, con
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_verify_run for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * launches, with the workspace taken from a buffer built into the library,
+ * MLA_VERIFY_NOALLOC_WORKSPACE_BYTES per GPU, which each GPU the library runs on
+ * holds from the first call on it until the process ends.  The arguments are
+ * those of mla_verify_run without the workspace.  A plan whose workspace_bytes
+ * exceeds the buffer is rejected with MLA_ERR_WORKSPACE before any device work.
+ * The call allocates nothing (its first call on a device locates that device's
+ * buffer).  Every call on one GPU uses the same buffer, which keeps the last
+ * call's status words and partials (nothing in it has to start at zero), so
+ * calls that overlap on one GPU race: calls on one stream are ordered, calls on
+ * different streams or threads must be ordered by the caller.  The status words
+ * of these calls are not readable by the caller (use mla_verify_run for them).
+ */
+#define MLA_VERIFY_NOALLOC_WORKSPACE_BYTES (64u << 20)
+mla_status mla_verify_run_noalloc(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                                  const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                                  const int32_t* kv_indices, const int32_t* tree_parents, float scale,
+                                  float* out, float* lse, void* stream);
+
+/*
  * The two halves of mla_verify_run, for callers that schedule or time them
  * separately. mla_verify_attend takes exactly the arguments of mla_verify_run
  * and enqueues the attention kernel: sequences with one KV split write out/lse

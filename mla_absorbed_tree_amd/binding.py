@@ -28,7 +28,7 @@ MLA_TREE_ACCEPT_MAX_TREE = 256
 
 # Symbols declared in include/*.h.
 EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
-                    "mla_verify_run_varlen",
+                    "mla_verify_run_varlen", "mla_verify_run_noalloc",
                     "mla_verify_attend", "mla_verify_combine",
                     "mla_verify_tree_masks", "mla_verify_plan_destroy",
                     "mla_verify_status_string", "mla_verify_last_error", "mla_kv_compact",
@@ -62,6 +62,15 @@ def _load():
         raise ImportError("libmlaverify.so is not built (expected at %s); run "
                           "`python -m mla_absorbed_tree_amd.build_lib` or __graft_entry__.build()"
                           % _LIB_PATH)
+    # One HIP runtime per process: torch wheels ship their own libamdhip64
+    # (soname libamdhip64.so.7, opened by the unversioned name). Loaded first,
+    # torch's copy also serves this library's libamdhip64.so.7 dependency;
+    # loaded after it, torch would open a second runtime next to the one this
+    # library pulled in, and launches on torch's memory would fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.mla_verify_plan.argtypes = [ctypes.POINTER(mla_verify_problem), ctypes.POINTER(vp),
@@ -70,6 +79,7 @@ def _load():
     lib.mla_verify_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                    ctypes.c_size_t, vp]
     lib.mla_verify_attend.argtypes = lib.mla_verify_run.argtypes
+    lib.mla_verify_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.mla_verify_run_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                           ctypes.c_size_t, vp]
     lib.mla_verify_combine.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -83,6 +93,7 @@ def _load():
     lib.mla_verify_last_error.argtypes = []
     lib.mla_verify_last_error.restype = ctypes.c_char_p
     for name in ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run", "mla_verify_run_varlen",
+                 "mla_verify_run_noalloc",
                  "mla_verify_attend", "mla_verify_combine", "mla_verify_tree_masks",
                  "mla_verify_plan_destroy", "mla_kv_compact", "mla_tree_accept",
                  "mla_tree_accept_packed"):
@@ -186,6 +197,17 @@ def mla_verify_run_varlen(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices,
                                       _ptr(kv_indptr), _ptr(kv_indices), _ptr(tree_indptr),
                                       _ptr(tree_parents), float(scale), _ptr(out), _ptr(lse),
                                       _ptr(workspace), int(workspace_bytes), _stream_handle(stream)))
+
+
+def mla_verify_run_noalloc(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents,
+                           scale: float, out, lse, stream=None) -> None:
+    """mla_verify_run with the library's built-in workspace (no workspace argument)."""
+    _check(_lib.mla_verify_run_noalloc(plan, _ptr(q_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe),
+                                       _ptr(kv_indptr), _ptr(kv_indices), _ptr(tree_parents),
+                                       float(scale), _ptr(out), _ptr(lse), _stream_handle(stream)))
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 def mla_verify_attend(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents,

@@ -172,6 +172,24 @@ mla_status mla_verify_run_varlen(mla_verify_plan_t plan, const void* q_nope, con
   return launch_combine(plan->plan, a, stream);
 }
 
+mla_status mla_verify_run_noalloc(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
+                                  const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
+                                  const int32_t* kv_indices, const int32_t* tree_parents, float scale,
+                                  float* out, float* lse, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(MLA_ERR_INVALID_ARG, "plan is NULL");
+  const size_t need = plan->plan.ws_bytes, cap = mlav::noalloc_scratch_bytes();
+  if (need > cap)
+    return fail(MLA_ERR_WORKSPACE, "the plan needs " + std::to_string(need) +
+                                       " bytes of workspace; the built-in buffer of mla_verify_run_noalloc holds " +
+                                       std::to_string(cap));
+  void* ws = nullptr;
+  const int e = mlav::noalloc_scratch(&ws);
+  if (e != 0) return fail(MLA_ERR_HIP, "locating the built-in workspace failed (hipError " + std::to_string(e) + ")");
+  return mla_verify_run(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents, scale, out, lse, ws,
+                        cap, stream);
+}
+
 mla_status mla_verify_attend(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
                              const void* kv_c, const void* k_pe, const int32_t* kv_indptr,
                              const int32_t* kv_indices, const int32_t* tree_parents, float scale,

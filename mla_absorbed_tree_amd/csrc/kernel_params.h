@@ -51,6 +51,11 @@ struct VerifyArgs {
 // Launchers (defined in the HIP translation unit). Return the launch error.
 int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks, void* stream);
 int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream);
+// Built-in workspace of mla_verify_run_noalloc (defined with the kernels):
+// its size, and its device address on the current device (0 on success, else
+// the hipError_t of locating it).
+size_t noalloc_scratch_bytes();
+int noalloc_scratch(void** ptr);
 int launch_tree_masks(const int32_t* parents, int32_t batch, int32_t tree_nodes, uint64_t* masks,
                       void* stream);  // masks [batch, tree_nodes, ceil(tree_nodes / 64)]
 // indptr NULL: trees of T nodes each; else packed trees of at most T nodes.

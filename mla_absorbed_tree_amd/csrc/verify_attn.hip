@@ -35,6 +35,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1249,6 +1250,39 @@ int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream) {
     hipLaunchKernelGGL(mla_verify_combine_kernel<float>, dim3((unsigned)groups), dim3(kCombineThreads), 0,
                        (hipStream_t)stream, a);
   return (int)hipGetLastError();
+}
+
+// ===========================================================================
+// Built-in workspace of mla_verify_run_noalloc
+// ===========================================================================
+// For callers that cannot allocate device memory: a file-scope device array
+// that every such call on a GPU shares; each GPU holds its own copy from the
+// first call on it until the process ends. In host code the array's name is
+// only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to a kernel.
+constexpr size_t kNoAllocScratchBytes = size_t(MLA_VERIFY_NOALLOC_WORKSPACE_BYTES);
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return 0;
 }
 
 int launch_tree_masks(const int32_t* parents, int32_t batch, int32_t tree_nodes, uint64_t* masks,

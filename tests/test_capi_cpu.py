@@ -201,3 +201,20 @@ def test_varlen_run_requires_tree_indptr(B):
                                 stream=0)
     assert e.value.status == B.MLA_ERR_INVALID_ARG
     B.mla_verify_plan_destroy(p)
+
+
+def test_noalloc_rejects_plans_beyond_its_buffer(B):
+    """mla_verify_run_noalloc checks the plan's workspace against its built-in
+    buffer before any device work (so this runs without a GPU)."""
+    # 8 sequences x 64 nodes x 64 heads, 64 forced splits of 64k keys: about
+    # 2 GB of split partials, far beyond the 64 MiB buffer.
+    plan, ws = B.mla_verify_plan(8, 64, 64, B.MLA_DTYPE_BF16, [65536] * 8, num_splits=64)
+    try:
+        assert ws > B.NOALLOC_WORKSPACE_BYTES
+        with pytest.raises(B.MlaVerifyError) as e:
+            B.mla_verify_run_noalloc(plan, None, None, None, None, None, None, None, 0.07, None, None,
+                                     stream=0)
+        assert e.value.status == B.MLA_ERR_WORKSPACE
+        assert "built-in buffer" in str(e.value)
+    finally:
+        B.mla_verify_plan_destroy(plan)

@@ -22,6 +22,10 @@ MLA_ERR_WORKSPACE = -3
 MLA_ERR_HIP = -4
 MLA_DTYPE_F32 = 0
 MLA_DTYPE_BF16 = 1
+# Per-sequence status words (int32 [batch] at workspace offset 0).
+MLA_VERIFY_STATUS_BAD_PARENT = 1
+MLA_VERIFY_STATUS_SHORT_KV = 2
+MLA_VERIFY_STATUS_TREE_RANGE = 4
 MLA_VERIFY_MAX_BATCH = 256
 MLA_VERIFY_MAX_TREE = 256
 MLA_TREE_ACCEPT_MAX_TREE = 256

@@ -106,7 +106,8 @@ typedef struct {
   int32_t keys_per_tile;    /* keys staged in LDS per step */
   int32_t grid_blocks;      /* workgroups of the attention launch */
   int32_t uses_combine;     /* 1 when a split-combine launch follows */
-  int32_t splits_per_workgroup; /* consecutive splits one workgroup runs (row block fixed) */
+  int32_t splits_per_workgroup; /* consecutive splits one workgroup runs (row block fixed),
+                                   merged in its accumulators into one partial */
   size_t workspace_bytes;   /* same value mla_verify_plan() returned */
 } mla_verify_plan_info;
 
@@ -212,14 +213,18 @@ mla_status mla_verify_run_noalloc(mla_verify_plan_t plan, const void* q_nope, co
 /*
  * The two halves of mla_verify_run, for callers that schedule or time them
  * separately. mla_verify_attend takes exactly the arguments of mla_verify_run
- * and enqueues the attention kernel: sequences with one KV split write out/lse
- * directly, the others leave per-split partials in the workspace: (m, l) in
- * fp32, and the split's unnormalised output O = l * o_split in the problem
+ * and enqueues the attention kernel. One workgroup runs a split group:
+ * splits_per_workgroup consecutive KV splits of one row block, which share
+ * one reference max, so their merge is a plain sum kept in the workgroup's
+ * accumulators. Sequences with a single split group write out/lse directly;
+ * the others leave one partial per split group in the workspace: (m, l) in
+ * fp32, and the group's unnormalised output O = l * o_group in the problem
  * dtype (fp32 for fp32 problems; bf16 for bf16 problems, whose rounding,
- * <= 2^-9 relative per element, moves the result by <= 2^-9 max |o_split|,
+ * <= 2^-9 relative per element, moves the result by <= 2^-9 max |o_group|,
  * far below the bf16 tolerance).
  * mla_verify_combine then merges those partials by log-sum-exp into out/lse
- * (it enqueues nothing when the plan has no split sequence). Calling attend and
+ * (it enqueues nothing when no sequence has more than one split group,
+ * uses_combine = 0). Calling attend and
  * then combine on one stream with the same workspace equals mla_verify_run.
  */
 mla_status mla_verify_attend(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,

@@ -24,11 +24,12 @@ struct VerifyArgs {
   const int32_t* tree_indptr;
   float* out;                  // [nodes, H, 512]
   float* lse;                  // [nodes, H] or nullptr
-  // Split partials [total_splits, part_rows, 512] (split launches only):
+  // Partials, one per split group [total_groups, part_rows, 512] (when some
+  // sequence has several groups; group_offset[b] is sequence b's first):
   // unnormalised O = sum of 2^(s - m) v, fp32 for fp32 problems, bf16 for
   // bf16 problems. Rows past a sequence's T_b * H are padding (never read).
   void* part_o;
-  float* part_ml;              // [total_splits, part_rows, 2]  (m in log2 units, l)
+  float* part_ml;              // [total_groups, part_rows, 2]  (m in log2 units, l)
   int32_t* status;             // [batch] per-sequence status words (MLA_VERIFY_STATUS_*)
   int64_t kv_c_stride;         // elements
   int64_t k_pe_stride;         // elements
@@ -44,7 +45,7 @@ struct VerifyArgs {
   // launch's arguments may take), which is what bounds the batch.
   int32_t split_offset[MLA_VERIFY_MAX_BATCH + 1];  // first global split of sequence b
   int32_t group;                                   // consecutive splits per workgroup
-  int32_t group_offset[MLA_VERIFY_MAX_BATCH + 1];  // first split group of sequence b
+  int32_t group_offset[MLA_VERIFY_MAX_BATCH + 1];  // first split group (and partial) of sequence b
   int32_t node_offset[MLA_VERIFY_MAX_BATCH + 1];   // first tree node of sequence b
 };
 

@@ -195,14 +195,16 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   for (int b = 0; b < p.batch; ++b) {
     plan.split_offset[b + 1] = plan.split_offset[b] + plan.splits[b];
     plan.max_splits = std::max(plan.max_splits, plan.splits[b]);
-    if (plan.splits[b] > 1) plan.combine = true;
   }
   plan.total_splits = plan.split_offset[p.batch];
   // Many short splits (a forced split count) would make thousands of
   // workgroups that each pay the fixed start-up and tail; instead one
   // workgroup runs several consecutive splits, aiming at about one workgroup
-  // per compute unit. The bf16 kernel only (the fp32 kernel runs one split);
-  // automatic splits are already sized for the chip (one split each).
+  // per compute unit. Its splits share one reference max, so their partials
+  // merge by a plain sum, done in the kernel's accumulators: the group writes
+  // one partial, and the combine merges the groups. The bf16 kernel only (the
+  // fp32 kernel runs one split per workgroup); automatic splits are already
+  // sized for the chip (one split each).
   plan.group = 1;
   if (p.dtype == MLA_DTYPE_BF16 && p.num_splits > 0) {
     int64_t split_row_blocks = 0;
@@ -214,6 +216,8 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   for (int b = 0; b < p.batch; ++b)
     plan.group_offset[b + 1] = plan.group_offset[b] + (plan.splits[b] + plan.group - 1) / plan.group;
   plan.total_groups = plan.group_offset[p.batch];
+  for (int b = 0; b < p.batch; ++b)
+    if (plan.group_offset[b + 1] - plan.group_offset[b] > 1) plan.combine = true;
   plan.chunk_groups = (plan.total_groups + kXcds - 1) / kXcds;
   plan.grid_blocks = int64_t(plan.chunk_groups) * kXcds * plan.row_blocks;
   if (plan.grid_blocks > (int64_t(1) << 31) - 1) {
@@ -225,9 +229,9 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   plan.ws_status = 0;
   size_t off = align_up(size_t(p.batch) * sizeof(int32_t), 256);
   if (plan.combine) {
-    // Partial rows per split padded to whole row blocks (the bf16 kernel
-    // stores unconditionally, padding rows included).
-    const size_t part_rows = size_t(plan.total_splits) * size_t(plan.row_blocks) * size_t(plan.rows_per_block);
+    // One partial per split group; rows padded to whole row blocks (the bf16
+    // kernel stores unconditionally, padding rows included).
+    const size_t part_rows = size_t(plan.total_groups) * size_t(plan.row_blocks) * size_t(plan.rows_per_block);
     plan.ws_part_ml = off;
     off = align_up(off + part_rows * 2 * sizeof(float), 256);
     plan.ws_part_o = off;

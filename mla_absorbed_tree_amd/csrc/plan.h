@@ -39,10 +39,10 @@ struct Plan {
   int32_t total_groups = 0;
   int32_t chunk_groups = 0;     // ceil(total_groups / kXcds)
   int64_t grid_blocks = 0;      // attention launch
-  bool combine = false;         // some sequence has S_b > 1
+  bool combine = false;         // some sequence has more than one split group
   // Workspace layout (byte offsets from the workspace start).
   size_t ws_status = 0;         // int32 [batch] status words (MLA_VERIFY_STATUS_*)
-  // Per (split, row), rows padded to row_blocks * rows_per_block per split:
+  // Per (split group, row), rows padded to row_blocks * rows_per_block per group:
   size_t ws_part_ml = 0;        // float2 (m in log2 units, l)
   size_t ws_part_o = 0;         // [512] unnormalised O: fp32, or bf16 for bf16 problems
   size_t ws_bytes = 0;

@@ -8,8 +8,9 @@
 // group of consecutive KV splits). Every key tile (kv_c | k_pe) is staged in
 // LDS once and serves all query rows of the block, so the head-shared latent
 // is read from L2 once per block instead of once per head. A workgroup with
-// several splits streams their tiles through one pipeline and writes one
-// partial per split.
+// several splits streams their tiles through one pipeline against one
+// reference max, so merging their (m, l, O) is a plain sum, done in the
+// accumulators; it writes one partial for the group.
 //
 // bf16 kernel: 4 waves, 128 query rows, 32-key tiles.
 //   * A 3-deep LDS ring of key tiles is filled by global_load_lds_dwordx4
@@ -142,8 +143,9 @@ __global__ void __launch_bounds__(kTreeMaskThreads) mla_tree_masks_kernel(const 
 struct BlockWork {
   int b, S, rb;
   int T, rows, node0;         // tree nodes of the sequence, T * H, its first packed node
-  int s, c;                   // current split: index within the sequence, global index
+  int s;                      // the group's first split (index within the sequence)
   int s_last;                 // one past the group's last split (within the sequence)
+  int G, part;                // split groups of the sequence; global index of this group's partial
   int kv0, N, P, ntiles;
   int tile_begin, tile_end;   // key tiles of the whole group
   bool seq_ok;
@@ -196,7 +198,8 @@ __device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w) {
   w.S = a.split_offset[w.b + 1] - a.split_offset[w.b];
   w.s = (cg - a.group_offset[w.b]) * a.group;
   w.s_last = min(w.s + a.group, w.S);
-  w.c = a.split_offset[w.b] + w.s;
+  w.G = a.group_offset[w.b + 1] - a.group_offset[w.b];
+  w.part = cg;
   w.kv0 = a.kv_indptr[w.b];
   w.N = a.kv_indptr[w.b + 1] - w.kv0;
   w.P = w.N - w.T;
@@ -297,13 +300,6 @@ constexpr int kAncBytes = kRows * kMaskWords * 8;             // ancestor mask w
 // operand fragments, [wave][fragment][lane] x 16 bytes.
 constexpr int kQpeBytes = kRows * kDr * 2;                     // 16384
 constexpr int kSmem = kNbuf * kBufBytes + kIdxBytes + kAncBytes + kQpeBytes;
-// Vector-memory stores one wave issues for a split partial: (m, l) plus
-// 16 feature blocks x 2 16-byte pieces. The wait after a split boundary lets
-// this many operations stay outstanding; it is safe as long as the compiler
-// emits at least this many store instructions, which holds because no two of
-// these stores are adjacent in memory (none can merge) and none is wider than
-// the widest store instruction.
-constexpr int kPartialStores = 1 + 16 * 2;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 // Trees above 64 nodes build their masks in the ring buffer of the third
 // tile, which is first loaded after the pipeline's first barrier.
@@ -587,11 +583,6 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // O^T of this wave's 32 rows: oacc[fb] holds features 32fb..32fb+31.
   f32x16_t oacc[16];
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
-  // Split boundaries inside the group: the weight sum of a tile that starts
-  // the next split stays out of l_run (it is still in sm.psum when the split
-  // ends, and starts the next split's sum).
-  bool next_starts_split = false;
-  const int s_first = w.s, c_first = w.c;
 
   // Invisible keys of one S^T block get -inf (register i holds key
   // k0 + (i/4)*8 + 4*half + i%4): keys from jend on, and tail keys (from P
@@ -656,7 +647,7 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         for (int jj = 0; jj < 8; ++jj) pw[u][jj] = (__bf16)sc[8 * u + jj];
       }
     } else if constexpr (k == 26) {
-      if (!next_starts_split) l_run += sm.psum;
+      l_run += sm.psum;
     }
   };
   constexpr int kStepsUsed = 27;
@@ -664,17 +655,16 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // A tile needs masking when it reaches the tree tail (or the sequence end).
   auto needs_mask = [&](int k0) { return k0 + kKeysPerTile > w.P; };
 
-  // Partial of global split c (sequences with several splits): (m, l) of this
+  // Partial c of the sequence's split groups (sequences with several groups): (m, l) of this
   // lane's row (both lanes of a row hold the same values) and its raw O in
   // bf16 (half the bytes of fp32; the rounding is relative to each partial and
   // averages out in the merge). Each wave writes only its own rows, so no
   // exchange and no barrier. Accumulator register i of block fb holds feature
   // 32fb + (i/4)*8 + 4*half + i%4 of the lane's row.
   //
-  // The partial arrays have a.part_rows (a multiple of kRows) rows per split,
-  // so the rows past T_b * H of the last row block have room and every
-  // store below is unconditional: exactly kPartialStores vector-memory
-  // instructions, which the wait after a split boundary relies on.
+  // The partial arrays have a.part_rows (a multiple of kRows) rows per
+  // group, so the rows past T_b * H of the last row block have room and every
+  // store below is unconditional.
   auto emit_partial = [&](int c, float l_part) {
     // Lane indices taken afresh (an opaque copy), so that no address below is
     // computed ahead of the tile loop and kept live through it.
@@ -733,7 +723,6 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 
   for (int pass = 0; pass < 2; ++pass) {
     l_run = 0.f;
-    next_starts_split = false;
     bool overflow = false;
 
     if (w.tile_begin < w.tile_end) {
@@ -791,27 +780,19 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       // Byte offsets of the buffers of tiles t, t+1 and t+2, rotated each
       // iteration (tile t+3 reuses the buffer of tile t).
       int bo0 = (tb % kNbuf) * kBufBytes, bo1 = ((tb + 1) % kNbuf) * kBufBytes, bo2 = ((tb + 2) % kNbuf) * kBufBytes;
-      int tile = tb;
-      // The splits of the group (at least one), one after the other; the
-      // tile pipeline runs on across their boundaries.
-      int sp = s_first;
-      do {
+      // The group's splits are consecutive ranges of key tiles: one stream
+      // through the pipeline.
 #pragma unroll
       for (int x = 0; x < 16; ++x)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
-      const int split_begin = tile, split_end = split_tile(sp + 1, w.ntiles, w.S);
-      for (; tile < split_end; ++tile) {
+      for (int tile = tb; tile < te; ++tile) {
         // Everything this wave issued in the previous iteration (the keys of
-        // tile+1 and the index block of tile+1+kIdxLead) has landed. After a
-        // split boundary the partial's stores, issued after those loads, may
-        // still be on their way.
-        if (tile == split_begin && sp != s_first) wait_vmem<kPartialStores>();
-        else wait_vmem<0>();
+        // tile+1 and a page-table batch) has landed.
+        wait_vmem<0>();
         const char* const vbase = smem + bo0 + v_off;  // tile t (PV)
         const char* const kbuf = smem + bo1;           // tile t+1 (QK)
         const bool has_next = tile + 1 < te;
-        next_starts_split = tile + 1 == split_end && has_next;
         const int k1 = (tile + 1) * kKeysPerTile;
         // Operand of MFMA j of the iteration: a V^T fragment of tile t (two
         // transpose reads) or a K fragment of tile t+1.
@@ -896,20 +877,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         bo1 = bo2;
         bo2 = bt;
       }
-      // Split sp is complete: its partial goes out (a redo pass rewrites
-      // it), and the weight sum of the next split's first tile, taken in the
-      // last iteration, starts the next sum. A split can be empty when the
-      // sequence is shorter than the plan assumed: its partial has l = 0 and
-      // O = 0, and the carried sum waits for the next split with tiles.
-      if (w.S > 1) {
-        if (split_end > split_begin) {
-          emit_partial(c_first + (sp - s_first), l_run);
-          l_run = sm.psum;
-        } else {
-          emit_partial(c_first + (sp - s_first), 0.f);
-        }
-      }
-      } while (++sp < w.s_last);
+      // The group's partial goes out (a redo pass rewrites it).
+      if (w.G > 1) emit_partial(w.part, l_run);
       wait_vmem<0>();
     } else {
       // No key tiles: empty partials (m = -inf, l = 0, O = 0).
@@ -917,15 +886,14 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       for (int x = 0; x < 16; ++x)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
-      if (w.S > 1)
-        for (int sp = s_first; sp < w.s_last; ++sp) emit_partial(c_first + (sp - s_first), 0.f);
+      if (w.G > 1) emit_partial(w.part, 0.f);
     }
     if (pass == 1 || !__syncthreads_or(overflow)) break;
     m_ref = m_max;
   }
 
-  // ---- epilogue: a sequence with one split writes its output -------------
-  if (w.S == 1) emit_final();
+  // ---- epilogue: a sequence with one split group writes its output -------
+  if (w.G == 1) emit_final();
 }
 
 // ===========================================================================
@@ -1082,12 +1050,12 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
   if (!row_ok) return;
   float* dst;
   float mul;
-  if (w.S == 1) {
+  if (w.G == 1) {
     dst = a.out + grow * kDl;
     mul = node_ok ? 1.f / l_tot : NAN;
     if (half == 0 && a.lse) a.lse[grow] = node_ok ? (m_ref + __log2f(l_tot)) * kLn2 : NAN;
   } else {
-    const int64_t prow = (int64_t)w.c * a.part_rows + r_eff;
+    const int64_t prow = (int64_t)w.part * a.part_rows + r_eff;
     dst = (float*)a.part_o + prow * kDl;
     mul = 1.f;
     if (half == 0) {
@@ -1109,15 +1077,14 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
 // ===========================================================================
 // Split combine
 // ===========================================================================
-// Merge the split partials of kCombineRows consecutive query rows of one
-// sequence: M = max m_c, w_c = 2^(m_c - M), L = sum w_c l_c,
+// Merge the partials (one per split group) of kCombineRows consecutive query
+// rows of one sequence: M = max m_c, w_c = 2^(m_c - M), L = sum w_c l_c,
 // out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Partials O_c are fp32 (fp32
-// problems) or bf16 (bf16 problems). Each row
-// has 4 groups of 32 lanes (16 features per lane); group g sums the splits
-// c = g (mod 4), and the groups' sums meet in LDS. The rows of a workgroup
-// are adjacent in every split's partial block. Empty splits (m = -inf) get
-// weight 0 (their partial is zeros); a NaN partial (invalid tree) makes the
-// row NaN.
+// problems) or bf16 (bf16 problems). Each row has 4 lane groups of 32 lanes
+// (16 features per lane); lane group g sums the partials c = g (mod 4), and
+// their sums meet in LDS. The rows of a workgroup are adjacent in every
+// partial block. Empty partials (m = -inf, or l = 0 and O = 0) get weight 0;
+// a NaN partial (invalid tree) makes the row NaN.
 constexpr int kCombineRows = 2;
 constexpr int kCombineGroups = 4;
 constexpr int kCombineThreads = 32 * kCombineGroups * kCombineRows;
@@ -1137,8 +1104,8 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   const int tid = threadIdx.x;
   const int j = tid / (32 * kCombineGroups), grp = (tid >> 5) % kCombineGroups, t32 = tid & 31;
   const int r = (int)(blockIdx.x % row_groups) * kCombineRows + j;
-  const int s0 = a.split_offset[b];
-  const int S = a.split_offset[b + 1] - s0;
+  const int s0 = a.group_offset[b];
+  const int S = a.group_offset[b + 1] - s0;
   // Whole workgroup: no split partials, or every row past this sequence's rows.
   if (S <= 1 || (int)(blockIdx.x % row_groups) * kCombineRows >= rows) return;
   const bool live = r < rows;

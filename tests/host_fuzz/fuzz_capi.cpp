@@ -48,7 +48,7 @@ void check_args(const mlav::VerifyArgs& a) {
   }
   check(a.part_rows >= a.max_rows_per_seq, "partial rows cover every sequence");
   if (a.part_o) {
-    const size_t rows = size_t(a.total_splits) * size_t(a.part_rows);
+    const size_t rows = size_t(a.group_offset[a.batch]) * size_t(a.part_rows);  // one per split group
     const uintptr_t o = reinterpret_cast<uintptr_t>(a.part_o), ml = reinterpret_cast<uintptr_t>(a.part_ml);
     check(ml >= g_ws + 4 * size_t(a.batch), "partials after the status words");
     check(ml + rows * 8 <= o, "(m, l) before O");

@@ -72,8 +72,9 @@ def test_forced_and_auto_split_schedules(B):
     # one workgroup per compute unit
     assert info["splits_per_workgroup"] == 16
     assert info["grid_blocks"] == 256 // 16 * (rows // info["rows_per_block"])
-    # per (split, row): fp32 (m, l) and the bf16 partial output
-    assert ws >= 256 * rows * (2 * 4 + 512 * 2)
+    # one partial per workgroup's group of 16 splits (their merge is a sum
+    # in the accumulators): per (group, row) fp32 (m, l) and the bf16 output
+    assert 16 * rows * (2 * 4 + 512 * 2) <= ws < 17 * rows * (2 * 4 + 512 * 2)
     B.mla_verify_plan_destroy(p)
     # groups that do not divide the split counts: 3 splits per workgroup,
     # ceil(40/3) + ceil(32/3) + ceil(40/3) = 14 + 11 + 14 groups, padded to 8 XCDs
@@ -206,9 +207,11 @@ def test_varlen_run_requires_tree_indptr(B):
 def test_noalloc_rejects_plans_beyond_its_buffer(B):
     """mla_verify_run_noalloc checks the plan's workspace against its built-in
     buffer before any device work (so this runs without a GPU)."""
-    # 8 sequences x 64 nodes x 64 heads, 64 forced splits of 64k keys: about
-    # 2 GB of split partials, far beyond the 64 MiB buffer.
-    plan, ws = B.mla_verify_plan(8, 64, 64, B.MLA_DTYPE_BF16, [65536] * 8, num_splits=64)
+    # fp32, 8 sequences x 64 nodes x 64 heads, 64 forced splits of 64k keys:
+    # the fp32 kernel writes one partial per split, about 4 GB, far beyond the
+    # 64 MiB buffer. (The bf16 kernel merges a workgroup's splits in its
+    # accumulators, so the same bf16 plan needs no partials at all.)
+    plan, ws = B.mla_verify_plan(8, 64, 64, B.MLA_DTYPE_F32, [65536] * 8, num_splits=64)
     try:
         assert ws > B.NOALLOC_WORKSPACE_BYTES
         with pytest.raises(B.MlaVerifyError) as e:

@@ -70,7 +70,8 @@ def test_noalloc_matches_run_on_two_calls_in_a_row():
 def test_noalloc_rejects_a_plan_beyond_the_buffer():
     from mla_absorbed_tree_amd import binding as B
 
-    plan, ws = B.mla_verify_plan(8, 64, 64, B.MLA_DTYPE_BF16, [65536] * 8, num_splits=64)
+    # fp32 writes one partial per split: about 4 GB here
+    plan, ws = B.mla_verify_plan(8, 64, 64, B.MLA_DTYPE_F32, [65536] * 8, num_splits=64)
     try:
         assert ws > B.NOALLOC_WORKSPACE_BYTES
         with pytest.raises(B.MlaVerifyError) as e:

@@ -12,21 +12,27 @@
 // reference max, so merging their (m, l, O) is a plain sum, done in the
 // accumulators; it writes one partial for the group.
 //
-// bf16 kernel: 4 waves, 128 query rows, 32-key tiles.
+// bf16 kernel: 4 waves (one per SIMD), 128 query rows, 32-key tiles.
 //   * A 3-deep LDS ring of key tiles is filled by global_load_lds_dwordx4
 //     (global -> LDS without registers); the loads of tile t+2 go out while
-//     tiles t and t+1 are computed on.
+//     tiles t and t+1 are computed on. Page-table entries travel the same
+//     way, eight tiles per load.
 //   * QK: wave w owns query rows 32w..32w+31 and keeps the latent 512
 //     features of their Q in VGPRs (the rope 64 in LDS). S^T[32 keys x 32
-//     rows] = K . Q^T with 36 mfma_f32_32x32x16_bf16.
+//     rows] = K . Q^T with 36 mfma_f32_32x32x16_bf16 whose accumulator stays
+//     in VGPRs.
 //   * Softmax weights in fp32 (exp2 domain) against a per-row reference max,
-//     rounded to bf16 and shared through LDS (P, 8 KB per tile).
-//   * PV: wave w owns output features 128w..128w+127 of all 128 rows:
-//     O^T[128 x 128] += V^T . P^T with 32 MFMAs; V^T comes from the same LDS
-//     tile through ds_read_b64_tr_b16, P^T with plain 16-byte LDS reads.
-//     Splitting PV by features (not rows) cuts the transpose reads, whose LDS
-//     rate is a third of plain reads, by 4x.
-//   * O^T lives in 256 accumulation registers per lane.
+//     computed by the row's own wave and spread between the MFMAs of the
+//     next tile's PV; rounded to bf16 as the P^T operand.
+//   * PV: waves 2i and 2i+1 form a pair; wave w accumulates feature half w%2
+//     (256 features) of O^T for its own 32 rows and for its partner's, so
+//     each V^T fragment (two ds_read_b64_tr_b16) feeds two MFMAs. The
+//     partner's P^T arrives through LDS (2 KB per wave and tile).
+//   * O^T lives in the 256 accumulation registers of each lane.
+// One wave streams about one LDS read per 24 cycles whatever its width
+// (measured), so the number of operand reads per MFMA matters more than LDS
+// bandwidth: 36 K + 4 rope-Q + 32 V^T + 2 P^T reads per wave and tile
+// against 68 MFMAs of 32 cycles.
 // The key order inside each 16-deep MFMA step is permuted consistently in P^T
 // and V^T so that P^T comes straight from the S^T accumulator layout.
 //
@@ -299,45 +305,97 @@ constexpr int kAncBytes = kRows * kMaskWords * 8;             // ancestor mask w
 // The rope part of Q (64 features of each row) as each lane's four MFMA
 // operand fragments, [wave][fragment][lane] x 16 bytes.
 constexpr int kQpeBytes = kRows * kDr * 2;                     // 16384
-constexpr int kSmem = kNbuf * kBufBytes + kIdxBytes + kAncBytes + kQpeBytes;
+
+// The P^T fragments of a tile pass between the two waves of a pair (waves
+// 2i and 2i+1) through LDS: [tile parity][wave][key step][lane] x 16 bytes.
+constexpr int kPxWaveBytes = 2 * 64 * 16;
+constexpr int kPxBytes = 2 * 4 * kPxWaveBytes;                // 16384
+// Row sums exchanged for the final normalisation, one float per row.
+constexpr int kLxBytes = kRows * 4;
+constexpr int kSmem = kNbuf * kBufBytes + kIdxBytes + kAncBytes + kQpeBytes + kPxBytes + kLxBytes;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 // Trees above 64 nodes build their masks in the ring buffer of the third
 // tile, which is first loaded after the pipeline's first barrier.
 static_assert(kTreeScratchBytes <= kBufBytes, "tree mask scratch");
 
-// MFMA order of one pipeline iteration (tile t in LDS for PV, tile t+1 for
-// QK): the first kPvHead PV MFMAs of tile t, whose operands are read before
-// the barrier, cover the latency of the first key reads of tile t+1; then the
-// 36 QK MFMAs of tile t+1 (4 rope, 32 latent chunks); then the other 28 PV
-// MFMAs, which the softmax of tile t+1 runs beside. PV MFMA (u, fb): key step u
-// (16 keys) of output feature block fb (32 features).
-constexpr int kPvHead = 4;
+// One pipeline iteration (tile t in LDS for PV, tile t+1 for QK) issues 68
+// MFMAs. PV is split between the two waves of a pair by output features:
+// wave w keeps O^T of feature half w%2 (256 features) for its own 32 rows
+// and for its partner's, so each V^T fragment (two transpose reads) feeds two
+// MFMAs: one with this wave's weights P^T, one with the partner's, read from
+// LDS after the barrier. PV operand p (0..15) is key step p/8 (16 keys) of
+// feature block p%8 of the half. Order: own-row PV of operands 0..2 (their
+// V^T read before the barrier), partner-row PV of the same operands (the
+// partner's P^T has arrived by then), the 36 QK MFMAs of tile t+1 (4 rope,
+// 32 latent chunks), then own and partner PV of operands 3..15, beside which
+// the softmax of tile t+1 runs.
+constexpr int kPvHead = 3;               // operands whose MFMAs open the iteration
 constexpr int kQkOps = 36;
-constexpr int kOps = kQkOps + 32;
-// Operand reads are issued kAhead MFMAs before their MFMA (a ring of
-// kAhead + 1 fragments).
-constexpr int kAhead = 4;
-constexpr int kRing = kAhead + 1;
-static_assert(kAhead <= kPvHead, "the reads issued before the barrier must be of tile t");
+constexpr int kPvOps = 32;
+constexpr int kOps = kQkOps + kPvOps;
+constexpr int kQk0 = 2 * kPvHead;        // slot of the first QK MFMA
 struct Op {
   bool pv;
-  int u, fb;  // PV: key step, feature block
-  int c;      // QK: 0..3 rope chunks, 4..35 latent chunks 0..31
+  bool partner;  // PV: the partner's rows
+  int p;         // PV: operand (key step p/8, feature block p%8 of the half)
+  int c;         // QK: 0..3 rope chunks, 4..35 latent chunks 0..31
+  int r;         // operand read (fragment) this MFMA consumes
 };
 __host__ __device__ constexpr Op iter_op(int j) {
-  return j < kPvHead ? Op{true, 0, j, 0}
-                     : j < kPvHead + kQkOps ? Op{false, 0, 0, j - kPvHead}
-                                             : Op{true, (j - kQkOps) >> 4, (j - kQkOps) & 15, 0};
+  if (j < kPvHead) return Op{true, false, j, 0, j};
+  if (j < kQk0) return Op{true, true, j - kPvHead, 0, j - kPvHead};
+  if (j < kQk0 + kQkOps) return Op{false, false, 0, j - kQk0, kPvHead + j - kQk0};
+  const int i = j - kQk0 - kQkOps;  // 0..25: operands kPvHead.., own then partner
+  return Op{true, (i & 1) != 0, kPvHead + (i >> 1), 0, kPvHead + kQkOps + (i >> 1)};
 }
+// Operand reads: kReads fragments per iteration, read r going to ring entry
+// r % kRing. Read r is issued kAhead reads ahead of its first use, but not
+// before the last use of the ring entry's previous fragment; reads 0..kPvHead-1
+// (V^T of tile t) before the barrier, the QK reads (tile t+1) after it.
+constexpr int kReads = kPvHead + kQkOps + (kPvOps / 2 - kPvHead);  // 52
+constexpr int kAhead = 4;
+constexpr int kRing = 6;
+constexpr int kPreBarrier = -2, kPostBarrier = -1;
+__host__ __device__ constexpr int first_use(int r) {
+  for (int j = 0; j < kOps; ++j)
+    if (iter_op(j).r == r) return j;
+  return kOps;
+}
+__host__ __device__ constexpr int last_use(int r) {
+  int u = -3;
+  for (int j = 0; j < kOps; ++j)
+    if (iter_op(j).r == r) u = j;
+  return u;
+}
+__host__ __device__ constexpr int issue_slot(int r) {
+  if (r < kPvHead) return kPreBarrier;
+  int s = kPostBarrier;
+  if (r >= kAhead && first_use(r - kAhead) > s) s = first_use(r - kAhead);
+  if (r >= kRing && last_use(r - kRing) + 1 > s) s = last_use(r - kRing) + 1;
+  return s;
+}
+__host__ __device__ constexpr bool schedule_ok() {
+  for (int r = 0; r < kReads; ++r) {
+    if (issue_slot(r) >= first_use(r)) return false;                           // read before use
+    if (r >= kRing && issue_slot(r) <= last_use(r - kRing)) return false;      // ring entry free
+    if (r >= kPvHead && r < kPvHead + kQkOps && issue_slot(r) < kPostBarrier) return false;
+  }
+  for (int j = 0; j < kOps; ++j)
+    if (iter_op(j).r < 0 || iter_op(j).r >= kReads) return false;
+  return true;
+}
+static_assert(schedule_ok(), "operand read schedule");
+static_assert(kRing > kPvHead, "the pre-barrier reads fit the ring");
 // Slots (MFMA indices) of the other work of an iteration: the loads of tile
 // t+2 (one part every third QK MFMA, the page-table block with the first),
-// the softmax of tile t+1 (after its last QK MFMA has left the pipe), and the
-// address preparation of tile t+3's loads.
-constexpr int kDmaSlot0 = kPvHead + 2, kDmaStride = 3;
-constexpr int kSoftmaxSlot0 = kPvHead + kQkOps;
-constexpr int kSoftmaxSteps = 28;
-constexpr int kPrepSlots[3] = {kPvHead + kQkOps + 1, kPvHead + kQkOps + 12, kPvHead + kQkOps + 22};
-static_assert(kDmaSlot0 + kDmaStride * 8 < kPvHead + kQkOps, "loads go out during QK");
+// the softmax of tile t+1 (after its last QK MFMA has left the pipe), the
+// hand-over of its weights to the partner, and the address preparation of
+// tile t+3's loads.
+constexpr int kDmaSlot0 = kQk0 + 2, kDmaStride = 3;
+constexpr int kSoftmaxSlot0 = kQk0 + kQkOps;
+constexpr int kSoftmaxSteps = 26;
+constexpr int kPrepSlots[3] = {kQk0 + kQkOps + 1, kQk0 + kQkOps + 12, kQk0 + kQkOps + 22};
+static_assert(kDmaSlot0 + kDmaStride * 8 < kQk0 + kQkOps, "loads go out during QK");
 static_assert(kSoftmaxSlot0 + kSoftmaxSteps <= kOps, "softmax fits the PV MFMAs");
 }  // namespace bf16k
 
@@ -478,6 +536,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   char* const idx_ring = smem + kNbuf * kBufBytes;
   uint64_t* const anc_lds = (uint64_t*)(idx_ring + kIdxBytes);
   char* const qpe_lds = idx_ring + kIdxBytes + kAncBytes;
+  char* const px_lds = qpe_lds + kQpeBytes;
+  float* const lx_lds = (float*)(px_lds + kPxBytes);
 
   BlockWork w;
   if (!map_block(a, w)) return;
@@ -489,6 +549,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;  // uniform: keep it scalar
   const int half = lane >> 5;   // k slice of MFMA operands / key quartet of S^T rows
   const int qcol = lane & 31;   // column of the 32x32 blocks: this lane's query row
+  const int partner = wave ^ 1;  // the wave whose rows share this wave's V^T reads
+  const int fhalf = wave & 1;    // output features 256*fhalf.. of both waves' rows
 
   // The page-table entries of the first two batches of tiles go out first,
   // so that their round trip overlaps the loads of Q and of the tree.
@@ -548,9 +610,10 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     const uint64_t* m = anc_lds + i * kMaskWords;
     return mask_window(u0, m[w0], w0 + 1 < kMaskWords ? m[w0 + 1] : 0ull);
   };
-  // Whether this lane's row belongs to a valid node (its mask is not empty).
-  auto row_valid = [&]() {
-    int i = wave * 32 + qcol;
+  // Whether row 32*wv + (lane%32) of the block belongs to a valid node (its
+  // mask is not empty).
+  auto row_valid = [&](int wv) {
+    int i = wv * 32 + qcol;
     asm volatile("" : "+v"(i));
     uint64_t any = 0;
 #pragma unroll
@@ -571,17 +634,27 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
   // 16*(g%2) + 4*(i%4) of the feature block. Lane l then holds feature l%32
   // of the block for keys 4*half + 0..3 (+8 for the second read). Feature
   // block fb of those keys: chunk 4*fb + 2*(g%2) + (i%4)/2, at byte 8*(i%2) of
-  // it, in the region of the keys' wave (plus 512*fb).
+  // it, in the region of the keys' wave (plus 512*fb); this wave's feature
+  // half starts at block 8*fhalf.
   const int g16 = lane >> 4, i16 = lane & 15;
   const int v_off = 256 * (g16 & 1) + 128 * ((i16 & 3) >> 1) +
-                    16 * ((4 * half + (i16 >> 2)) ^ kvc_swizzle(2 * (g16 & 1))) + 8 * (i16 & 1);
+                    16 * ((4 * half + (i16 >> 2)) ^ kvc_swizzle(2 * (g16 & 1))) + 8 * (i16 & 1) +
+                    fhalf * 8 * 512;
+  // P^T fragments: this lane's slot in this wave's and in the partner's area.
+  char* const px_own = px_lds + wave * kPxWaveBytes + lane * 16;
+  const char* const px_partner = px_lds + partner * kPxWaveBytes + lane * 16;
+  // Weights of a tile (parity tp) for the partner: fragment u at u*1024.
+  auto write_p = [&](const bf16x8_t& frag, int u, int tp) {
+    *(bf16x8_t*)(px_own + tp * 4 * kPxWaveBytes + u * 1024) = frag;
+  };
 
   // Softmax state of this lane's row (same rules as the fp32 kernel):
   // m_ref = reference max (log2 units, scaled) fixed at the first tile where
   // the row sees a key; weights are 2^(s - m_ref); if some score exceeds it by
   // more than kOverflowSlack the block repeats the split with the exact max.
-  // O^T of this wave's 32 rows: oacc[fb] holds features 32fb..32fb+31.
-  f32x16_t oacc[16];
+  // O^T of feature half fhalf: oacc[0][fb] for this wave's 32 rows,
+  // oacc[1][fb] for the partner's, features 256*fhalf + 32fb..+31.
+  f32x16_t oacc[2][8];
   float m_ref = -INFINITY, m_max = -INFINITY, l_run = 0.f;
 
   // Invisible keys of one S^T block get -inf (register i holds key
@@ -646,21 +719,21 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) pw[u][jj] = (__bf16)sc[8 * u + jj];
       }
-    } else if constexpr (k == 26) {
-      l_run += sm.psum;
+      if constexpr (i == 17) l_run += sm.psum;
     }
   };
-  constexpr int kStepsUsed = 27;
+  constexpr int kStepsUsed = 26;
   static_assert(kSoftmaxSteps >= kStepsUsed, "softmax steps");
   // A tile needs masking when it reaches the tree tail (or the sequence end).
   auto needs_mask = [&](int k0) { return k0 + kKeysPerTile > w.P; };
 
-  // Partial c of the sequence's split groups (sequences with several groups): (m, l) of this
-  // lane's row (both lanes of a row hold the same values) and its raw O in
-  // bf16 (half the bytes of fp32; the rounding is relative to each partial and
-  // averages out in the merge). Each wave writes only its own rows, so no
-  // exchange and no barrier. Accumulator register i of block fb holds feature
-  // 32fb + (i/4)*8 + 4*half + i%4 of the lane's row.
+  // Partial c of the sequence's split groups (sequences with several
+  // groups): (m, l) of this wave's rows (both lanes of a row hold the same
+  // values), written by this wave, and the raw O in bf16 (half the bytes of
+  // fp32; the rounding is relative to each partial and averages out in the
+  // merge), of which this wave holds feature half fhalf of its own and its
+  // partner's rows. Nothing is exchanged, so no barrier. Accumulator register
+  // i of block fb holds feature 256*fhalf + 32fb + (i/4)*8 + 4*half + i%4.
   //
   // The partial arrays have a.part_rows (a multiple of kRows) rows per
   // group, so the rows past T_b * H of the last row block have room and every
@@ -672,58 +745,81 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     asm volatile("" : "+v"(lq));
     const int qcol = lq & 31, half = lq >> 5;
     const float l_tot = l_part + swap_halves(l_part);
-    const bool node_ok = row_valid();
+    const bool node_ok = row_valid(wave);
     mfma_result_wait();  // the last PV MFMAs may have just been issued
-    const int64_t prow = (int64_t)c * a.part_rows + w.rb * kRows + wave * 32 + qcol;
-    *(float2*)(a.part_ml + 2 * prow) = make_float2(node_ok ? m_ref : NAN, node_ok ? l_tot : NAN);
-    __bf16* dst = (__bf16*)a.part_o + prow * kDl + 8 * half;
+    const int64_t prow0 = (int64_t)c * a.part_rows + w.rb * kRows + qcol;
+    *(float2*)(a.part_ml + 2 * (prow0 + wave * 32)) = make_float2(node_ok ? m_ref : NAN, node_ok ? l_tot : NAN);
 #pragma unroll
-    for (int fb = 0; fb < 16; ++fb)
+    for (int rbk = 0; rbk < 2; ++rbk) {
+      const int64_t prow = prow0 + (rbk ? partner : wave) * 32;
+      __bf16* dst = (__bf16*)a.part_o + prow * kDl + fhalf * 256 + 8 * half;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        // Values 2m and 2m+1 (features 16m + 4*half + 0..3 and 16m + 8 +
-        // 4*half + 0..3 of the block) become 8 consecutive features per lane
-        // by one exchange between the wave halves: the lower half keeps
-        // 16m..16m+7, the upper half gets 16m+8..16m+15.
-        const f32x4_t t0 = read_acc4(oacc[fb], 2 * m);
-        const f32x4_t t1 = read_acc4(oacc[fb], 2 * m + 1);
-        uint32_t x[2], y[2];
+      for (int fb = 0; fb < 8; ++fb)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          x[e] = pack_bf16x2(t0[2 * e], t0[2 * e + 1]);
-          y[e] = pack_bf16x2(t1[2 * e], t1[2 * e + 1]);
-          const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
-          x[e] = sw[0];
-          y[e] = sw[1];
+        for (int m = 0; m < 2; ++m) {
+          // Values 2m and 2m+1 (features 16m + 4*half + 0..3 and 16m + 8 +
+          // 4*half + 0..3 of the block) become 8 consecutive features per
+          // lane by one exchange between the wave halves: the lower half
+          // keeps 16m..16m+7, the upper half gets 16m+8..16m+15.
+          const f32x4_t t0 = read_acc4(oacc[rbk][fb], 2 * m);
+          const f32x4_t t1 = read_acc4(oacc[rbk][fb], 2 * m + 1);
+          uint32_t x[2], y[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            x[e] = pack_bf16x2(t0[2 * e], t0[2 * e + 1]);
+            y[e] = pack_bf16x2(t1[2 * e], t1[2 * e + 1]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+            x[e] = sw[0];
+            y[e] = sw[1];
+          }
+          *(u32x4_t*)(dst + 32 * fb + 16 * m) = u32x4_t{x[0], x[1], y[0], y[1]};
+          // One pair at a time: otherwise the scheduler reads every
+          // accumulator out at once and runs out of registers.
+          __builtin_amdgcn_sched_barrier(0);
         }
-        *(u32x4_t*)(dst + 32 * fb + 16 * m) = u32x4_t{x[0], x[1], y[0], y[1]};
-        // One pair at a time: otherwise the scheduler reads every
-        // accumulator out at once and runs out of registers.
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    }
   };
-  // Output of a sequence with one split: O / l and lse of this lane's row.
+  // Output of a sequence with one split group: O / l and lse. The partner's
+  // row sums come through LDS (every wave of the workgroup calls this).
   auto emit_final = [&]() {
     const float l_tot = l_run + swap_halves(l_run);
-    const bool node_ok = row_valid();
+    if (half == 0) lx_lds[wave * 32 + qcol] = l_tot;
+    __syncthreads();
+    const float l_par = lx_lds[partner * 32 + qcol];
+    const bool ok_own = row_valid(wave), ok_par = row_valid(partner);
     mfma_result_wait();
-    if (r_local >= w.rows) return;
-    const int64_t g = (int64_t)w.node0 * H + r_local;
-    float* dst = a.out + g * kDl + 4 * half;
-    const float mul = node_ok ? 1.f / l_tot : NAN;
-    if (half == 0 && a.lse) a.lse[g] = node_ok ? (m_ref + __log2f(l_tot)) * kLn2 : NAN;
+    const int r_own = w.rb * kRows + wave * 32 + qcol, r_par = w.rb * kRows + partner * 32 + qcol;
+    if (r_own < w.rows && half == 0 && a.lse) {
+      const int64_t g = (int64_t)w.node0 * H + r_own;
+      a.lse[g] = ok_own ? (m_ref + __log2f(l_tot)) * kLn2 : NAN;
+    }
 #pragma unroll
-    for (int fb = 0; fb < 16; ++fb)
+    for (int rbk = 0; rbk < 2; ++rbk) {
+      const int r = rbk ? r_par : r_own;
+      if (r < w.rows) {
+        const int64_t g = (int64_t)w.node0 * H + r;
+        float* dst = a.out + g * kDl + fhalf * 256 + 4 * half;
+        const float mul = (rbk ? ok_par : ok_own) ? 1.f / (rbk ? l_par : l_tot) : NAN;
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const f32x4_t v = read_acc4(oacc[fb], gi);
-        *(f32x4_t*)(dst + 32 * fb + 8 * gi) = v * mul;
+        for (int fb = 0; fb < 8; ++fb)
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi) {
+            const f32x4_t v = read_acc4(oacc[rbk][fb], gi);
+            *(f32x4_t*)(dst + 32 * fb + 8 * gi) = v * mul;
+          }
       }
+    }
   };
 
   for (int pass = 0; pass < 2; ++pass) {
     l_run = 0.f;
     bool overflow = false;
+#pragma unroll
+    for (int rbk = 0; rbk < 2; ++rbk)
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[rbk][x][i] = 0.f;
 
     if (w.tile_begin < w.tile_end) {
       const int tb = w.tile_begin, te = w.tile_end;
@@ -731,10 +827,11 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       // Pipeline. Iteration t: tiles t and t+1 are in LDS, tile t+2 and the
       // page-table entries of t+2+kIdxLead are fetched; the QK and softmax
       // of tile t+1 run between the PV MFMAs of tile t, whose weights this
-      // wave computed in the previous iteration and holds in registers. The
-      // tiles past the group repeat its last key (loaded, never visible),
-      // which keeps the number of loads per iteration constant; the QK of
-      // the group's last iteration runs on such a tile and is masked out.
+      // wave computed in the previous iteration and holds in registers (the
+      // partner's arrive through LDS). The tiles past the group repeat its
+      // last key (loaded, never visible), which keeps the number of loads per
+      // iteration constant; the QK of the group's last iteration runs on
+      // such a tile and is masked out.
       if (pass > 0) {  // pass 0 issued these at the start
         issue_index_batch(a, idx_ring, w.kv0, jmax, tb / kIdxBatch);
         issue_index_batch(a, idx_ring, w.kv0, jmax, tb / kIdxBatch + 1);
@@ -775,6 +872,8 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
         qk_result_wait(s0);
         if (needs_mask(tb * kKeysPerTile)) mask_tile(s0, tb * kKeysPerTile, w.N);
         static_for<kSoftmaxSteps>([&](auto k) { softmax_step(k, s0, pk, overflow); });
+        write_p(pk[0], 0, tb & 1);
+        write_p(pk[1], 1, tb & 1);
       }
 
       // Byte offsets of the buffers of tiles t, t+1 and t+2, rotated each
@@ -782,25 +881,24 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       int bo0 = (tb % kNbuf) * kBufBytes, bo1 = ((tb + 1) % kNbuf) * kBufBytes, bo2 = ((tb + 2) % kNbuf) * kBufBytes;
       // The group's splits are consecutive ranges of key tiles: one stream
       // through the pipeline.
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
       for (int tile = tb; tile < te; ++tile) {
         // Everything this wave issued in the previous iteration (the keys of
-        // tile+1 and a page-table batch) has landed.
+        // tile+1, a page-table batch, its weights for the partner) has landed.
         wait_vmem<0>();
+        wait_lds();
         const char* const vbase = smem + bo0 + v_off;  // tile t (PV)
         const char* const kbuf = smem + bo1;           // tile t+1 (QK)
         const bool has_next = tile + 1 < te;
         const int k1 = (tile + 1) * kKeysPerTile;
-        // Operand of MFMA j of the iteration: a V^T fragment of tile t (two
+        // Fragment r of the iteration: a V^T fragment of tile t (two
         // transpose reads) or a K fragment of tile t+1.
-        auto read_op = [&](auto jc) -> bf16x8_t {
-          constexpr Op o = iter_op(decltype(jc)::value);
+        auto read_op = [&](auto rc) -> bf16x8_t {
+          constexpr int r = decltype(rc)::value;
+          constexpr Op o = iter_op(first_use(r));
           if constexpr (o.pv) {
             // keys 16u + 4*half + 0..3 in region 2u, the next 8 keys in region 2u+1
-            const char* vp = vbase + 2 * o.u * kRegion + o.fb * 512;
+            constexpr int u = o.p >> 3, fb = o.p & 7;
+            const char* vp = vbase + 2 * u * kRegion + fb * 512;
             const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)vp);
             const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + kRegion));
             return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -811,31 +909,49 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
             return *(const bf16x8_t*)(kbuf + ((kc & 1) ? k_off1 : k_off0) + 1024 * (kc >> 2) + 256 * (kc & 3));
           }
         };
-        // Before the barrier: the rope part of Q (this lane's own LDS data,
-        // written once before the loop) and the operands of the first PV
-        // MFMAs (tile t has been visible since the previous barrier).
+        bf16x8_t ring[kRing];
+        auto issue_reads = [&](auto sc) {
+          constexpr int sl = decltype(sc)::value;
+          static_for<kReads>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            if constexpr (issue_slot(r) == sl) ring[r % kRing] = read_op(rc);
+          });
+        };
+        // Before the barrier: the V^T operands of the first PV MFMAs (tile t
+        // has been visible since the previous barrier).
+        issue_reads(std::integral_constant<int, kPreBarrier>{});
+        block_sync();  // tile+1 and the partner's weights of tile t are visible; every wave has finished with tile-1
+        bf16x8_t pp[2];
+        {
+          const char* src = px_partner + (tile & 1) * 4 * kPxWaveBytes;
+          pp[0] = *(const bf16x8_t*)src;
+          pp[1] = *(const bf16x8_t*)(src + 1024);
+        }
+        issue_reads(std::integral_constant<int, kPostBarrier>{});
+        // The rope part of Q (this lane's own LDS data, written once before
+        // the loop), for QK MFMAs 0..3.
         bf16x8_t qf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) qf[j] = *(const bf16x8_t*)(qpe_lane + j * 64 * 16);
-        bf16x8_t ring[kRing];
-        static_for<kAhead>([&](auto j) { ring[j % kRing] = read_op(j); });
-        block_sync();  // tile+1 is visible; every wave has finished with tile-1
         f32x16_t sacc;
         bf16x8_t pn[2];
         int pslots = 0, pkslot = 0;
         static_for<kOps>([&](auto sc) {
           constexpr int s = decltype(sc)::value;
-          if constexpr (s + kAhead < kOps)
-            ring[(s + kAhead) % kRing] = read_op(std::integral_constant<int, s + kAhead>{});
+          issue_reads(sc);
           constexpr Op o = iter_op(s);
           if constexpr (o.pv) {
-            oacc[o.fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[s % kRing], pk[o.u], oacc[o.fb], 0, 0, 0);
+            constexpr int u = o.p >> 3, fb = o.p & 7;
+            if constexpr (o.partner)
+              oacc[1][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[o.r % kRing], pp[u], oacc[1][fb], 0, 0, 0);
+            else
+              oacc[0][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[o.r % kRing], pk[u], oacc[0][fb], 0, 0, 0);
           } else if constexpr (o.c == 0) {
-            mfma_qk_first(sacc, ring[s % kRing], qf[0]);
+            mfma_qk_first(sacc, ring[o.r % kRing], qf[0]);
           } else if constexpr (o.c < 4) {
-            mfma_qk(sacc, ring[s % kRing], qf[o.c]);
+            mfma_qk(sacc, ring[o.r % kRing], qf[o.c]);
           } else {
-            mfma_qk(sacc, ring[s % kRing], qreg[o.c - 4]);
+            mfma_qk(sacc, ring[o.r % kRing], qreg[o.c - 4]);
           }
           // Tile t+2 goes into the buffer tile t-1 used; its addresses were
           // prepared during the previous iteration. One load every few QK
@@ -860,6 +976,10 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
           }
           if constexpr (s >= kSoftmaxSlot0 && s - kSoftmaxSlot0 < kSoftmaxSteps)
             softmax_step(std::integral_constant<int, s - kSoftmaxSlot0>{}, sacc, pn, overflow);
+          // Weights of tile t+1 for the partner, as soon as each fragment is
+          // complete (softmax steps 18 and 25).
+          if constexpr (s == kSoftmaxSlot0 + 19) write_p(pn[0], 0, (tile + 1) & 1);
+          if constexpr (s == kSoftmaxSlot0 + 25) write_p(pn[1], 1, (tile + 1) & 1);
           // Addresses of tile t+3's loads (entries landed before this
           // iteration's wait).
           if constexpr (s == kPrepSlots[0]) {
@@ -882,10 +1002,6 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
       wait_vmem<0>();
     } else {
       // No key tiles: empty partials (m = -inf, l = 0, O = 0).
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[x][i] = 0.f;
       if (w.G > 1) emit_partial(w.part, 0.f);
     }
     if (pass == 1 || !__syncthreads_or(overflow)) break;

@@ -12,7 +12,9 @@ and the token-acceptance launch that follows a verify step in "tree_accept".
 The paged workload (page_size = 1 pool of 600k slots) and a batch of packed
 trees of 1..256 nodes per sequence (32k prefix) are reported in "also" as well.
 
-Prints ONE JSON line. `value` is KV tokens/s (sum of N_b per step / step time);
+Prints ONE JSON line. `value` is KV tokens/s (sum of N_b per step / step time,
+the step time being the median of the timed steps' HIP-event durations; the
+mean and the host wall-clock mean are reported beside it);
 `roofline` describes the attention kernel (algorithmic FLOPs per launch over
 its average HIP-event duration, against the dense bf16 MFMA peak);
 `cpu_baseline` is the float64 oracle timed on the host on a bounded sample.
@@ -119,22 +121,38 @@ def bench_workload(name, steps, warmup, num_splits=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     attn_each = [e[0].elapsed_time(e[1]) for e in events]
+    comb_each = [e[1].elapsed_time(e[2]) for e in events]
+    step_each = [e[0].elapsed_time(e[2]) for e in events]
     attn_ms = float(np.mean(attn_each))
-    comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    step_ms = wall / steps * 1e3
+    comb_ms = float(np.mean(comb_each))
+    wall_ms = wall / steps * 1e3
+    # The step time t is the median over the timed steps of one step's
+    # HIP-event duration (attention launch start to combine end).
+    step_ms = float(np.median(step_each))
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     achieved = flops / (attn_ms * 1e-3)
+    # Split partials: each (group, row) partial is written by the attention
+    # launch and read back by the combine: (m, l) in fp32 and O in the problem
+    # dtype.
+    part_elem = 2 if cfg.dtype == "bf16" else 4
+    partial_bytes = 2 * int(mv.info["partial_rows"]) * (2 * 4 + 512 * part_elem)
     res = {
         "workload": name,
         "value": kv_tokens / (step_ms * 1e-3),
         "ms_per_step": step_ms,
+        "ms_per_step_mean": float(np.mean(step_each)),
+        "ms_per_step_wall_mean": wall_ms,
         "kv_tokens": kv_tokens,
         "visible_pairs_per_s": pairs * cfg.heads / (step_ms * 1e-3),
+        "algorithmic_bytes": bytes_,
+        "partial_bytes": partial_bytes,
         "hbm_gbps": bytes_ / (step_ms * 1e-3) / 1e9,
+        "hbm_gbps_with_partials": (bytes_ + partial_bytes) / (step_ms * 1e-3) / 1e9,
         "hbm_frac": bytes_ / (step_ms * 1e-3) / PEAK_HBM_BYTES,
         "mfma_frac": flops / (step_ms * 1e-3) / PEAK_BF16_FLOPS,
         "kernels_ms": {"attention": attn_ms, "combine": comb_ms,
-                       "attention_median": float(np.median(attn_each))},
+                       "attention_median": float(np.median(attn_each)),
+                       "combine_median": float(np.median(comb_each))},
         "plan": mv.info,
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS, "traffic": measured_traffic(name),
@@ -151,6 +169,64 @@ def bench_workload(name, steps, warmup, num_splits=None):
     del d
     torch.cuda.empty_cache()
     return res, x
+
+
+def bench_redo(x, steps, warmup, positions=(5000, 25000)):
+    """Cost of the softmax redo on the primary workload: every query along one
+    direction, once as drawn (no score leaves the first tile's reference max
+    by more than the slack) and once with one key of each split planted 40x
+    longer along that direction (every workgroup takes the second pass).
+    Returns the step times of the two and their ratio."""
+    import copy
+    import torch
+    from gen.inputs import round_to_bf16
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+
+    cfg = x.cfg
+    rng = np.random.default_rng(11)
+    direction = rng.standard_normal(576).astype(np.float32)
+    direction /= np.linalg.norm(direction)
+    y = copy.copy(x)
+    y.q_nope = round_to_bf16(np.ascontiguousarray(np.broadcast_to(5.0 * direction[:512], x.q_nope.shape),
+                                                  dtype=np.float32))
+    y.q_pe = round_to_bf16(np.ascontiguousarray(np.broadcast_to(5.0 * direction[512:], x.q_pe.shape),
+                                                dtype=np.float32))
+    spikes = [int(x.kv_indices[int(x.kv_indptr[b]) + p]) for b in range(cfg.batch) for p in positions]
+    rows = int(x.tree_indptr[-1])
+    out = torch.empty((rows, cfg.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows, cfg.heads), dtype=torch.float32, device="cuda")
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, cfg.num_splits)
+    times = {}
+    for label, planted in (("normal", False), ("redo", True)):
+        saved = [(x.kv_c[s].copy(), x.k_pe[s].copy()) for s in spikes]
+        if planted:  # on the host copy only while it is uploaded
+            for s_ in spikes:
+                x.kv_c[s_] = round_to_bf16(np.ascontiguousarray(200.0 * direction[:512], dtype=np.float32))
+                x.k_pe[s_] = round_to_bf16(np.ascontiguousarray(200.0 * direction[512:], dtype=np.float32))
+        y.kv_c, y.k_pe = x.kv_c, x.k_pe
+        d = device_inputs(y)
+        for s_, (c, pe) in zip(spikes, saved):
+            x.kv_c[s_], x.k_pe[s_] = c, pe
+        call = lambda: mv(d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"], d["kv_indices"],
+                          d["tree_parents"], x.scale, out=out, lse=lse)
+        for _ in range(warmup):
+            call()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            call()
+            e[1].record()
+        torch.cuda.synchronize()
+        times[label] = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        assert torch.isfinite(out).all()
+        del d
+    mv.close()
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "normal_ms": times["normal"], "redo_ms": times["redo"],
+            "ratio": times["redo"] / times["normal"],
+            "setup": "queries along one direction; one key of each split %s planted in the redo case"
+                     % (list(positions),)}
 
 
 def bench_kv_compact(steps, warmup, name="b8_h64_paged600k_t16_bf16"):
@@ -359,13 +435,17 @@ def main():
     if not a.no_also and a.workload == PRIMARY:
         for name in (ALSO, PAGED, RAGGED):
             r2, _ = bench_workload(name, a.steps, a.warmup)
-            also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "visible_pairs_per_s",
-                                            "hbm_gbps", "hbm_frac", "mfma_frac", "kernels_ms", "roofline",
-                                            "config", "plan")})
-    compact = accept = None
+            also.append({k: r2[k] for k in ("workload", "value", "ms_per_step", "ms_per_step_mean",
+                                            "ms_per_step_wall_mean", "visible_pairs_per_s",
+                                            "algorithmic_bytes", "partial_bytes", "hbm_gbps",
+                                            "hbm_gbps_with_partials", "hbm_frac", "mfma_frac", "kernels_ms",
+                                            "roofline", "config", "plan")})
+    compact = accept = redo = None
     if not a.no_also and not a.no_compact:
         compact = bench_kv_compact(a.steps, a.warmup)
         accept = bench_tree_accept(a.steps, a.warmup)
+    if not a.no_also and a.workload == PRIMARY:
+        redo = bench_redo(x, min(a.steps, 10), min(a.warmup, 3))
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the float64 oracle on a bounded sample")
@@ -379,6 +459,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": res["ms_per_step"],
+        "ms_per_step_mean": res["ms_per_step_mean"],
+        "ms_per_step_wall_mean": res["ms_per_step_wall_mean"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -386,7 +468,10 @@ def main():
         "data": "synthetic",
         "config": res["config"],
         "visible_pairs_per_s": res["visible_pairs_per_s"],
+        "algorithmic_bytes": res["algorithmic_bytes"],
+        "partial_bytes": res["partial_bytes"],
         "hbm_gbps": res["hbm_gbps"],
+        "hbm_gbps_with_partials": res["hbm_gbps_with_partials"],
         "hbm_frac": res["hbm_frac"],
         "mfma_frac": res["mfma_frac"],
         "kernels_ms": res["kernels_ms"],
@@ -396,6 +481,7 @@ def main():
         "also": also,
         "kv_compact": compact,
         "tree_accept": accept,
+        "softmax_redo": redo,
     }
     print(json.dumps(line), flush=True)
 

@@ -108,7 +108,11 @@ typedef struct {
   int32_t uses_combine;     /* 1 when a split-combine launch follows */
   int32_t splits_per_workgroup; /* consecutive splits one workgroup runs (row block fixed),
                                    merged in its accumulators into one partial */
+  int32_t total_groups;     /* sum over sequences of their split groups */
   size_t workspace_bytes;   /* same value mla_verify_plan() returned */
+  int64_t partial_rows;     /* (group, query row) partials one run writes and the
+                               combine reads back: sum over sequences with more
+                               than one group of groups * T_b * num_heads */
 } mla_verify_plan_info;
 
 /*

@@ -58,7 +58,8 @@ class mla_verify_plan_info(ctypes.Structure):
     _fields_ = [("total_splits", ctypes.c_int32), ("max_splits", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("keys_per_tile", ctypes.c_int32),
                 ("grid_blocks", ctypes.c_int32), ("uses_combine", ctypes.c_int32),
-                ("splits_per_workgroup", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("splits_per_workgroup", ctypes.c_int32), ("total_groups", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t), ("partial_rows", ctypes.c_int64)]
 
 
 def _load():

@@ -60,7 +60,9 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
   info->grid_blocks = int32_t(p.grid_blocks);
   info->uses_combine = p.combine ? 1 : 0;
   info->splits_per_workgroup = p.group;
+  info->total_groups = p.total_groups;
   info->workspace_bytes = p.ws_bytes;
+  info->partial_rows = p.partial_rows;
   return MLA_OK;
 }
 

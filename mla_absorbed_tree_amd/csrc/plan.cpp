@@ -216,8 +216,13 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   for (int b = 0; b < p.batch; ++b)
     plan.group_offset[b + 1] = plan.group_offset[b] + (plan.splits[b] + plan.group - 1) / plan.group;
   plan.total_groups = plan.group_offset[p.batch];
-  for (int b = 0; b < p.batch; ++b)
-    if (plan.group_offset[b + 1] - plan.group_offset[b] > 1) plan.combine = true;
+  for (int b = 0; b < p.batch; ++b) {
+    const int32_t g = plan.group_offset[b + 1] - plan.group_offset[b];
+    if (g > 1) {
+      plan.combine = true;
+      plan.partial_rows += int64_t(g) * plan.tree_len[b] * p.num_heads;
+    }
+  }
   plan.chunk_groups = (plan.total_groups + kXcds - 1) / kXcds;
   plan.grid_blocks = int64_t(plan.chunk_groups) * kXcds * plan.row_blocks;
   if (plan.grid_blocks > (int64_t(1) << 31) - 1) {

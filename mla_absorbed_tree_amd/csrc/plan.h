@@ -33,10 +33,12 @@ struct Plan {
   std::vector<int32_t> split_offset;  // [batch + 1] prefix sums of S_b
   int32_t total_splits = 0, max_splits = 0;
   // A workgroup runs `group` consecutive splits of one sequence for one row
-  // block (one stream of key tiles, a partial written at each split end).
+  // block: one stream of key tiles against one reference max, merged in its
+  // accumulators, one partial per group.
   int32_t group = 1;
   std::vector<int32_t> group_offset;  // [batch + 1] prefix sums of ceil(S_b / group)
   int32_t total_groups = 0;
+  int64_t partial_rows = 0;     // sum over sequences with > 1 group of groups * T_b * H
   int32_t chunk_groups = 0;     // ceil(total_groups / kXcds)
   int64_t grid_blocks = 0;      // attention launch
   bool combine = false;         // some sequence has more than one split group

@@ -192,6 +192,19 @@ def test_plans_of_the_named_workloads(B):
         info = B.mla_verify_plan_get_info(p)
         B.mla_verify_plan_destroy(p)
         assert (info["total_splits"], info["grid_blocks"], info["splits_per_workgroup"]) == (splits, grid, group), name
+        # A workgroup merges `group` consecutive splits into one partial:
+        # groups per sequence = ceil(S_b / group). With equal splits per
+        # sequence (every workload here but the paged and ragged ones, which
+        # run one split per group), partial_rows = sum of G_b * T_b * H over
+        # the sequences with more than one group.
+        if group == 1:
+            assert info["total_groups"] == info["total_splits"], name
+        if info["total_splits"] % cfg.batch == 0 and info["max_splits"] * cfg.batch == info["total_splits"]:
+            g = -(-info["max_splits"] // group)
+            assert info["total_groups"] == g * cfg.batch, name
+            T = Tb if Tb is not None else np.full(cfg.batch, cfg.tree_nodes)
+            assert info["partial_rows"] == (g * int(np.sum(T)) * cfg.heads if g > 1 else 0), name
+            assert info["uses_combine"] == int(g > 1), name
 
 
 def test_varlen_run_requires_tree_indptr(B):

@@ -252,6 +252,41 @@ def test_repeat_runs_are_bitwise_identical():
     np.testing.assert_array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("name,reps", [("b4_h64_p32768_t64_bf16", 24), ("b1_h64_p200000_t32_bf16_s256", 16),
+                                       ("b4_h64_p32768_t1to256_ragged_bf16", 8)])
+def test_stress_back_to_back_runs_are_bitwise_stable(name, reps):
+    """Many runs of one plan enqueued back to back on one stream, with no
+    synchronisation between them (each run's workgroups overlap the previous
+    run's tail), at full size in the benchmark's launch configuration: every
+    run's out and lse equal the first run's bit for bit. The LDS ring, the
+    barrier per tile, the weight exchange between paired waves and the split
+    groups must not let any data race show through."""
+    import torch
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+    cfg = get_config(name)
+    x = make_inputs(cfg)
+    d = device_inputs(x)
+    ragged = x.parents.ndim == 1
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, cfg.num_splits,
+                   tree_lens=x.tree_lens if ragged else None)
+    rows = int(x.tree_indptr[-1])
+    outs = [torch.empty((rows, cfg.heads, 512), dtype=torch.float32, device="cuda") for _ in range(2)]
+    lses = [torch.empty((rows, cfg.heads), dtype=torch.float32, device="cuda") for _ in range(2)]
+    args = (d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"], d["kv_indices"], d["tree_parents"],
+            x.scale)
+    log("  %s: %d runs back to back, plan %s" % (name, reps, mv.info))
+    mv(*args, out=outs[0], lse=lses[0])
+    mismatches = torch.zeros((), dtype=torch.int64, device="cuda")
+    for _ in range(reps - 1):
+        mv(*args, out=outs[1], lse=lses[1])
+        # compared on the stream, so no run waits for the host
+        mismatches += (outs[1] != outs[0]).sum() + (lses[1] != lses[0]).sum()
+    torch.cuda.synchronize()
+    mv.close()
+    assert torch.isfinite(outs[0]).all() and torch.isfinite(lses[0]).all()
+    assert int(mismatches) == 0
+
+
 # --------------------------------------------------------------------------
 # tree masks and invalid trees
 # --------------------------------------------------------------------------

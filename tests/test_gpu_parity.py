@@ -145,6 +145,31 @@ def test_split_groups_late_spike_redo():
     assert np.abs(o[:cfg.tree_nodes] - x.kv_c[spike]).max() < 0.05  # sequence 0
 
 
+@pytest.mark.parametrize("dtype,splits", [("bf16", 4), ("bf16", 8), ("f32", 6), ("bf16", 12), ("f32", 20)])
+def test_plan_for_longer_kv_leaves_empty_split_groups(dtype, splits):
+    """A plan built for 4000-key sequences runs on much shorter ones (plan
+    reuse across decode steps): the run divides each sequence's actual tiles
+    among the planned splits, so the later split groups get no key and write
+    empty partials (m = -inf). Up to 8 groups per row the one-wave-per-row
+    combine merges them, above that the lane-group combine; both must weigh
+    the empty ones to nothing."""
+    import torch
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+    base = "b1_h64_p4096_t16_bf16" if dtype == "bf16" else "tiny_f32_b1_h16_p256_t8"
+    cfg = get_config(base, batch=3, heads=16, tree_nodes=8, prefix=None, prefix_range=(1, 70), seed=77)
+    x = make_inputs(cfg)
+    d = device_inputs(x)
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, np.full(cfg.batch, 4000), splits)
+    assert mv.info["total_groups"] == cfg.batch * splits and mv.info["uses_combine"] == 1, mv.info
+    o, lse = mv(d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"], d["kv_indices"], d["tree_parents"],
+                x.scale)
+    torch.cuda.synchronize()
+    mv.close()
+    log("  kv lens %s, plan %s" % (list(x.kv_lens), mv.info))
+    o_ref, lse_ref = run_oracle(x)
+    compare(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dtype, "(%d splits)" % splits)
+
+
 def test_interleaved_576_wide_cache():
     """kv_c and k_pe inside one [slots, 576] buffer via row strides."""
     import torch

@@ -824,8 +824,9 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     if (w.tile_begin < w.tile_end) {
       const int tb = w.tile_begin, te = w.tile_end;
       const int jmax = min(w.N, te * kKeysPerTile) - 1;
-      // Pipeline. Iteration t: tiles t and t+1 are in LDS, tile t+2 and the
-      // page-table entries of t+2+kIdxLead are fetched; the QK and softmax
+      // Pipeline. Iteration t: tiles t and t+1 are in LDS, tile t+2 is
+      // fetched (and, when t+kIdxLead starts a batch, the page-table entries
+      // of tiles t+kIdxLead..t+kIdxLead+7); the QK and softmax
       // of tile t+1 run between the PV MFMAs of tile t, whose weights this
       // wave computed in the previous iteration and holds in registers (the
       // partner's arrive through LDS). The tiles past the group repeat its

@@ -53,8 +53,9 @@ double estimate_launch(const std::vector<int64_t>& tiles, const std::vector<int6
 
 // Automatic split counts: candidate chunk lengths ceil(max_tiles / k),
 // k = 1, 2, ..., no shorter than kMinChunkTiles (a split's partial costs
-// about a few tiles); S_b = ceil(tiles_b / chunk). The estimate decides; a
-// candidate must beat the best so far by 1% (ties keep fewer splits).
+// about a few tiles); S_b = ceil(tiles_b / chunk), each candidate also tried
+// with its total raised to a multiple of the XCD count. The estimate decides;
+// a candidate must beat the best so far by 1% (ties keep fewer splits).
 // Shorter chunks only add workgroups, so the search stops at the first
 // candidate with more than kMaxSearchWorkgroups of them (beyond one split per
 // sequence): by then the chip runs many even rounds and finer chunks buy
@@ -87,6 +88,34 @@ std::vector<int32_t> choose_auto_splits(const std::vector<int64_t>& tiles,
     if (best_t < 0.0 || t < 0.99 * best_t) {
       best_t = t;
       best = cand;
+    }
+    // The same candidate with its split count raised to a multiple of the
+    // XCD count (one more split at a time for the sequence whose splits are
+    // longest), so that every XCD gets as many split groups.
+    std::vector<int32_t> even = cand;
+    int64_t total = 0;
+    for (int32_t x : even) total += x;
+    bool grown = false;
+    while (total % kXcds != 0) {
+      size_t arg = tiles.size();
+      int64_t longest = 0;
+      for (size_t b = 0; b < tiles.size(); ++b) {
+        // no chunk below kMinChunkTiles
+        if (even[b] == 0 || (tiles[b] + even[b]) / (even[b] + 1) < kMinChunkTiles) continue;
+        const int64_t len = (tiles[b] + even[b] - 1) / even[b];
+        if (len > longest) longest = len, arg = b;
+      }
+      if (arg == tiles.size()) break;  // no sequence can take another split
+      ++even[arg];
+      ++total;
+      grown = true;
+    }
+    if (grown) {
+      const double te = estimate_launch(tiles, row_blocks, even, rows_per_block, dtype);
+      if (te < 0.99 * best_t) {
+        best_t = te;
+        best = even;
+      }
     }
   }
   return best;

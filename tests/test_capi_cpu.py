@@ -179,7 +179,7 @@ def test_plans_of_the_named_workloads(B):
     from gen import get_config, make_inputs
     want = {"tiny_f32_b1_h16_p256_t8": (2, 32, 1), "b1_h64_p4096_t16_bf16": (17, 192, 1),
             "b4_h64_p32768_t64_bf16": (8, 256, 1), "b1_h64_p200000_t32_bf16_s256": (256, 256, 16),
-            "b8_h64_paged600k_t16_bf16": (92, 768, 1), "b4_h64_p32768_t1to256_ragged_bf16": (32, 3328, 1)}
+            "b8_h64_paged600k_t16_bf16": (64, 512, 1), "b4_h64_p32768_t1to256_ragged_bf16": (32, 3328, 1)}
     for name, (splits, grid, group) in want.items():
         cfg = get_config(name)
         rng = np.random.default_rng(cfg.seed)  # only the lengths and tree sizes are needed

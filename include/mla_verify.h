@@ -157,7 +157,7 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
  *   lse         device fp32 [nodes, H] (natural log) or NULL
  *   workspace   device, >= workspace_bytes of the plan, 256-byte aligned.  Holds
  *               the status words (MLA_VERIFY_STATUS_*, int32 [batch] at offset
- *               0) and the split partials between the two launches; concurrent
+ *               0) and the split-group partials between the two launches; concurrent
  *               runs need separate workspaces.
  * No allocation, no host synchronisation, no memset and no host reads of
  * device data: the call only enqueues kernels, so it can be captured in a HIP

@@ -218,7 +218,8 @@ NOALLOC_WORKSPACE_BYTES = 64 << 20
 def mla_verify_attend(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents,
                       scale: float, out, lse, workspace, workspace_bytes: Optional[int] = None,
                       stream=None) -> None:
-    """Enqueue only the attention kernel (split sequences leave partials in the workspace)."""
+    """Enqueue only the attention kernel (sequences with several split groups leave one
+    partial per group in the workspace)."""
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.mla_verify_attend(plan, _ptr(q_nope), _ptr(q_pe), _ptr(kv_c), _ptr(k_pe),
@@ -229,7 +230,8 @@ def mla_verify_attend(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tre
 
 def mla_verify_combine(plan, out, lse, workspace, workspace_bytes: Optional[int] = None,
                        stream=None) -> None:
-    """Enqueue the log-sum-exp merge of the split partials (no-op without splits)."""
+    """Enqueue the log-sum-exp merge of the split-group partials (no-op when no sequence
+    has more than one group)."""
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.mla_verify_combine(plan, _ptr(out), _ptr(lse), _ptr(workspace),

@@ -49,7 +49,9 @@ typedef enum {
 
 typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
 
-/* Opaque, immutable after mla_verify_plan(); safe to share between threads. */
+/* Opaque. Immutable after mla_verify_plan() (and, for batches above
+   MLA_VERIFY_ARG_TABLE_BATCH, after mla_verify_plan_stage_tables()); safe to
+   share between threads from then on. */
 typedef struct mla_verify_plan_s* mla_verify_plan_t;
 
 typedef struct {
@@ -77,10 +79,13 @@ typedef struct {
                                    item 3]. */
 } mla_verify_problem;
 
-/* The batch bound comes from kernel-argument space: the per-sequence split,
-   split-group and node offset tables (3 x (batch + 1) int32) travel in each
-   launch's argument block, whose size the launch limits to 4 KB. */
-#define MLA_VERIFY_MAX_BATCH 256
+/* Sequences per plan. */
+#define MLA_VERIFY_MAX_BATCH 65536
+/* The per-sequence split, split-group and node offset tables (3 x (batch + 1)
+   int32) travel in each launch's argument block for batches up to this size
+   (the block may hold 4 KB). Larger batches keep them in device memory that
+   the caller provides once, through mla_verify_plan_stage_tables(). */
+#define MLA_VERIFY_ARG_TABLE_BATCH 256
 /* Ancestor masks are four 64-bit words per node. */
 #define MLA_VERIFY_MAX_TREE 256
 
@@ -110,6 +115,9 @@ typedef struct {
                                    merged in its accumulators into one partial */
   int32_t total_groups;     /* sum over sequences of their split groups */
   size_t workspace_bytes;   /* same value mla_verify_plan() returned */
+  size_t table_bytes;       /* device bytes mla_verify_plan_stage_tables() needs:
+                               12 * (batch + 1) when batch > MLA_VERIFY_ARG_TABLE_BATCH,
+                               else 0 (the tables travel in the launch arguments) */
   int64_t partial_rows;     /* (group, query row) partials one run writes and the
                                combine reads back: sum over sequences with more
                                than one group of groups * T_b * num_heads */
@@ -126,6 +134,25 @@ mla_status mla_verify_plan(const mla_verify_problem* problem, mla_verify_plan_t*
 
 /* Describe a plan (host only). */
 mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info* info);
+
+/*
+ * Batches above MLA_VERIFY_ARG_TABLE_BATCH only: copy the plan's per-sequence
+ * tables (split, split-group and node offsets, int32 [3][batch + 1]) into
+ * caller-owned device memory and have every later run of the plan read them
+ * there. Call it once after mla_verify_plan() and before the plan's first
+ * run, from one thread: it enqueues one host-to-device copy on `stream` and
+ * records `tables` in the plan (not for graph capture; the runs it enables
+ * are). Runs on other streams must be ordered after that copy by the caller.
+ *   tables        device, >= table_bytes of mla_verify_plan_get_info(), 4-byte
+ *                 aligned; owned by the caller, left unchanged and alive as long
+ *                 as the plan runs.
+ *   tables_bytes  its size.
+ * For a plan whose tables fit the launch arguments it does nothing and
+ * returns MLA_OK. Runs of a larger plan fail with MLA_ERR_INVALID_ARG until it
+ * has been called.
+ */
+mla_status mla_verify_plan_stage_tables(mla_verify_plan_t plan, void* tables, size_t tables_bytes,
+                                        void* stream);
 
 /*
  * Tree-verify attention of one batch (device work on `stream`, asynchronous).

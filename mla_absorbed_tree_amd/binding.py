@@ -26,12 +26,14 @@ MLA_DTYPE_BF16 = 1
 MLA_VERIFY_STATUS_BAD_PARENT = 1
 MLA_VERIFY_STATUS_SHORT_KV = 2
 MLA_VERIFY_STATUS_TREE_RANGE = 4
-MLA_VERIFY_MAX_BATCH = 256
+MLA_VERIFY_MAX_BATCH = 65536
+MLA_VERIFY_ARG_TABLE_BATCH = 256
 MLA_VERIFY_MAX_TREE = 256
 MLA_TREE_ACCEPT_MAX_TREE = 256
 
 # Symbols declared in include/*.h.
-EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_run",
+EXPORTED_SYMBOLS = ("mla_verify_plan", "mla_verify_plan_get_info", "mla_verify_plan_stage_tables",
+                    "mla_verify_run",
                     "mla_verify_run_varlen", "mla_verify_run_noalloc",
                     "mla_verify_attend", "mla_verify_combine",
                     "mla_verify_tree_masks", "mla_verify_plan_destroy",
@@ -59,7 +61,8 @@ class mla_verify_plan_info(ctypes.Structure):
                 ("rows_per_block", ctypes.c_int32), ("keys_per_tile", ctypes.c_int32),
                 ("grid_blocks", ctypes.c_int32), ("uses_combine", ctypes.c_int32),
                 ("splits_per_workgroup", ctypes.c_int32), ("total_groups", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t), ("partial_rows", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_size_t), ("table_bytes", ctypes.c_size_t),
+                ("partial_rows", ctypes.c_int64)]
 
 
 def _load():
@@ -81,6 +84,7 @@ def _load():
     lib.mla_verify_plan.argtypes = [ctypes.POINTER(mla_verify_problem), ctypes.POINTER(vp),
                                     ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_verify_plan_get_info.argtypes = [vp, ctypes.POINTER(mla_verify_plan_info)]
+    lib.mla_verify_plan_stage_tables.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.mla_verify_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                    ctypes.c_size_t, vp]
     lib.mla_verify_attend.argtypes = lib.mla_verify_run.argtypes
@@ -178,6 +182,14 @@ def mla_verify_plan_get_info(plan) -> dict:
 
 def mla_verify_plan_destroy(plan) -> None:
     _check(_lib.mla_verify_plan_destroy(plan))
+
+
+def mla_verify_plan_stage_tables(plan, tables, tables_bytes: Optional[int] = None, stream=None) -> None:
+    """Copy a large batch's per-sequence tables to `tables` (device) once, before the plan's
+    first run (no-op for batches whose tables fit the launch arguments)."""
+    if tables_bytes is None:
+        tables_bytes = 0 if tables is None else tables.numel() * tables.element_size()
+    _check(_lib.mla_verify_plan_stage_tables(plan, _ptr(tables), int(tables_bytes), _stream_handle(stream)))
 
 
 def mla_verify_run(plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents,

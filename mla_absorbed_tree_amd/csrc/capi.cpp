@@ -5,6 +5,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/mla_kv_compact.h"
 #include "../../include/mla_tree_accept.h"
@@ -15,6 +16,11 @@
 
 struct mla_verify_plan_s {
   mlav::Plan plan;
+  // Batches above MLA_VERIFY_ARG_TABLE_BATCH: the per-sequence tables,
+  // [split_offset | group_offset | node_offset], as staged on the host and
+  // the caller's device copy (set by mla_verify_plan_stage_tables).
+  std::vector<int32_t> tables;
+  const int32_t* dev_tables = nullptr;
 };
 
 namespace {
@@ -45,8 +51,29 @@ mla_status mla_verify_plan(const mla_verify_problem* problem, mla_verify_plan_t*
     delete h;
     return fail(st, err);
   }
+  if (problem->batch > MLA_VERIFY_ARG_TABLE_BATCH) {
+    const mlav::Plan& p = h->plan;
+    h->tables.reserve(3 * size_t(p.batch + 1));
+    h->tables.insert(h->tables.end(), p.split_offset.begin(), p.split_offset.end());
+    h->tables.insert(h->tables.end(), p.group_offset.begin(), p.group_offset.end());
+    h->tables.insert(h->tables.end(), p.node_offset.begin(), p.node_offset.end());
+  }
   *out = h;
   *workspace_bytes = h->plan.ws_bytes;
+  return MLA_OK;
+}
+
+mla_status mla_verify_plan_stage_tables(mla_verify_plan_t plan, void* tables, size_t tables_bytes, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(MLA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->tables.empty()) return MLA_OK;  // the tables travel in the launch arguments
+  const size_t need = plan->tables.size() * sizeof(int32_t);
+  if (!tables || tables_bytes < need)
+    return fail(MLA_ERR_INVALID_ARG, "the plan's tables need " + std::to_string(need) + " bytes of device memory");
+  if ((reinterpret_cast<uintptr_t>(tables) & 3u) != 0) return fail(MLA_ERR_INVALID_ARG, "tables must be 4-byte aligned");
+  const int e = mlav::copy_tables_to_device(tables, plan->tables.data(), need, stream);
+  if (e != 0) return fail(MLA_ERR_HIP, "copying the tables failed (hipError " + std::to_string(e) + ")");
+  plan->dev_tables = static_cast<const int32_t*>(tables);
   return MLA_OK;
 }
 
@@ -62,6 +89,7 @@ mla_status mla_verify_plan_get_info(mla_verify_plan_t plan, mla_verify_plan_info
   info->splits_per_workgroup = p.group;
   info->total_groups = p.total_groups;
   info->workspace_bytes = p.ws_bytes;
+  info->table_bytes = plan->tables.size() * sizeof(int32_t);
   info->partial_rows = p.partial_rows;
   return MLA_OK;
 }
@@ -119,10 +147,19 @@ mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
   a.part_rows = p.row_blocks * p.rows_per_block;
   a.row_blocks = p.row_blocks;
   a.total_splits = p.total_splits;
-  for (int b = 0; b <= p.batch; ++b) a.split_offset[b] = p.split_offset[b];
   a.group = p.group;
-  for (int b = 0; b <= p.batch; ++b) a.group_offset[b] = p.group_offset[b];
-  for (int b = 0; b <= p.batch; ++b) a.node_offset[b] = p.node_offset[b];
+  a.max_groups = p.max_groups;
+  if (p.batch > MLA_VERIFY_ARG_TABLE_BATCH) {
+    if (!plan->dev_tables)
+      return fail(MLA_ERR_INVALID_ARG, "a plan of " + std::to_string(p.batch) +
+                                           " sequences needs its tables staged with mla_verify_plan_stage_tables");
+    a.dev_tables = plan->dev_tables;
+  } else {
+    a.dev_tables = nullptr;
+    for (int b = 0; b <= p.batch; ++b) a.split_offset[b] = p.split_offset[b];
+    for (int b = 0; b <= p.batch; ++b) a.group_offset[b] = p.group_offset[b];
+    for (int b = 0; b <= p.batch; ++b) a.node_offset[b] = p.node_offset[b];
+  }
   return MLA_OK;
 }
 

@@ -40,18 +40,25 @@ struct VerifyArgs {
   int32_t part_rows;           // row_blocks * rows per workgroup (>= max_rows_per_seq)
   int32_t row_blocks;          // workgroups along the rows of the largest tree
   int32_t total_splits;
-  // The per-sequence tables travel in the kernel-argument block (three
-  // tables of MLA_VERIFY_MAX_BATCH + 1 words, about 3 KB of the 4 KB that a
-  // launch's arguments may take), which is what bounds the batch.
-  int32_t split_offset[MLA_VERIFY_MAX_BATCH + 1];  // first global split of sequence b
   int32_t group;                                   // consecutive splits per workgroup
-  int32_t group_offset[MLA_VERIFY_MAX_BATCH + 1];  // first split group (and partial) of sequence b
-  int32_t node_offset[MLA_VERIFY_MAX_BATCH + 1];   // first tree node of sequence b
+  int32_t max_groups;                              // largest split-group count of one sequence
+  // The per-sequence tables. Batches of up to MLA_VERIFY_ARG_TABLE_BATCH
+  // carry them here, in the kernel-argument block (three tables of
+  // MLA_VERIFY_ARG_TABLE_BATCH + 1 words, about 3 KB of the 4 KB a launch's
+  // arguments may take); larger batches read them from device memory that
+  // mla_verify_plan_stage_tables filled: dev_tables = [split_offset |
+  // group_offset | node_offset], batch + 1 words each (nullptr otherwise).
+  const int32_t* dev_tables;
+  int32_t split_offset[MLA_VERIFY_ARG_TABLE_BATCH + 1];  // first global split of sequence b
+  int32_t group_offset[MLA_VERIFY_ARG_TABLE_BATCH + 1];  // first split group (and partial) of sequence b
+  int32_t node_offset[MLA_VERIFY_ARG_TABLE_BATCH + 1];   // first tree node of sequence b
 };
 
 // Launchers (defined in the HIP translation unit). Return the launch error.
 int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks, void* stream);
 int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream);
+// Host -> device copy of a plan's per-sequence tables (enqueued on stream).
+int copy_tables_to_device(void* dst, const void* src, size_t bytes, void* stream);
 // Built-in workspace of mla_verify_run_noalloc (defined with the kernels):
 // its size, and its device address on the current device (0 on success, else
 // the hipError_t of locating it).

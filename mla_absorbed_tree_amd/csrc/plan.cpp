@@ -247,6 +247,7 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   plan.total_groups = plan.group_offset[p.batch];
   for (int b = 0; b < p.batch; ++b) {
     const int32_t g = plan.group_offset[b + 1] - plan.group_offset[b];
+    plan.max_groups = std::max(plan.max_groups, g);
     if (g > 1) {
       plan.combine = true;
       plan.partial_rows += int64_t(g) * plan.tree_len[b] * p.num_heads;

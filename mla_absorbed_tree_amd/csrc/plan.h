@@ -38,6 +38,7 @@ struct Plan {
   int32_t group = 1;
   std::vector<int32_t> group_offset;  // [batch + 1] prefix sums of ceil(S_b / group)
   int32_t total_groups = 0;
+  int32_t max_groups = 0;       // largest group count of one sequence
   int64_t partial_rows = 0;     // sum over sequences with > 1 group of groups * T_b * H
   int32_t chunk_groups = 0;     // ceil(total_groups / kXcds)
   int64_t grid_blocks = 0;      // attention launch

@@ -166,9 +166,31 @@ __device__ __forceinline__ int split_tile(int s, int ntiles, int S) { return (in
 // outside 0..the planned size, a negative offset, or a tree ending past
 // tree_indptr[batch]) give an empty tree, so the sequence is skipped, and
 // return MLA_VERIFY_STATUS_TREE_RANGE; otherwise 0.
+// Per-sequence tables: from the argument block, or from device memory for
+// batches above MLA_VERIFY_ARG_TABLE_BATCH.
+// Every index is wave-uniform and the device tables are never written during
+// a launch, so they are read through the constant address space: scalar
+// loads, whose results stay in scalar registers like the argument block's.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int table_entry(const VerifyArgs& a, int t, int i) {
+  return ((const_i32_ptr)(uintptr_t)a.dev_tables)[t * (a.batch + 1) + i];
+}
+__device__ __forceinline__ int split_off(const VerifyArgs& a, int i) {
+  if (a.dev_tables) return table_entry(a, 0, i);
+  return a.split_offset[i];
+}
+__device__ __forceinline__ int group_off(const VerifyArgs& a, int i) {
+  if (a.dev_tables) return table_entry(a, 1, i);
+  return a.group_offset[i];
+}
+__device__ __forceinline__ int node_off(const VerifyArgs& a, int i) {
+  if (a.dev_tables) return table_entry(a, 2, i);
+  return a.node_offset[i];
+}
+
 __device__ __forceinline__ int seq_tree(const VerifyArgs& a, int b, int& node0, int& T) {
-  node0 = a.node_offset[b];
-  T = a.node_offset[b + 1] - node0;
+  node0 = node_off(a, b);
+  T = node_off(a, b + 1) - node0;
   if (a.tree_indptr) {
     const int cap = T;
     node0 = a.tree_indptr[b];
@@ -191,20 +213,20 @@ __device__ __forceinline__ bool map_block(const VerifyArgs& a, BlockWork& w) {
   const int local = bid / kXcds;
   w.rb = local % a.row_blocks;
   const int cg = (local / a.row_blocks) * kXcds + xcd;
-  if (cg >= a.group_offset[a.batch]) return false;
+  if (cg >= group_off(a, a.batch)) return false;
   int lo = 0, hi = a.batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (a.group_offset[mid] <= cg) lo = mid;
+    if (group_off(a, mid) <= cg) lo = mid;
     else hi = mid - 1;
   }
   w.b = lo;
   w.tree_status = seq_tree(a, w.b, w.node0, w.T);
   w.rows = w.T * a.heads;
-  w.S = a.split_offset[w.b + 1] - a.split_offset[w.b];
-  w.s = (cg - a.group_offset[w.b]) * a.group;
+  w.S = split_off(a, w.b + 1) - split_off(a, w.b);
+  w.s = (cg - group_off(a, w.b)) * a.group;
   w.s_last = min(w.s + a.group, w.S);
-  w.G = a.group_offset[w.b + 1] - a.group_offset[w.b];
+  w.G = group_off(a, w.b + 1) - group_off(a, w.b);
   w.part = cg;
   w.kv0 = a.kv_indptr[w.b];
   w.N = a.kv_indptr[w.b + 1] - w.kv0;
@@ -244,8 +266,8 @@ __device__ void write_status(const VerifyArgs& a, const BlockWork& w) {
     int n0, t2;
     return seq_tree(a, b2, n0, t2);
   };
-  for (int b2 = w.b - 1; b2 >= 0 && a.split_offset[b2 + 1] == a.split_offset[b2]; --b2) a.status[b2] = empty_status(b2);
-  if (a.split_offset[w.b + 1] == a.split_offset[a.batch])
+  for (int b2 = w.b - 1; b2 >= 0 && split_off(a, b2 + 1) == split_off(a, b2); --b2) a.status[b2] = empty_status(b2);
+  if (split_off(a, w.b + 1) == split_off(a, a.batch))
     for (int b2 = w.b + 1; b2 < a.batch; ++b2) a.status[b2] = empty_status(b2);
 }
 
@@ -1221,8 +1243,8 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   const int tid = threadIdx.x;
   const int j = tid / (32 * kCombineGroups), grp = (tid >> 5) % kCombineGroups, t32 = tid & 31;
   const int r = (int)(blockIdx.x % row_groups) * kCombineRows + j;
-  const int s0 = a.group_offset[b];
-  const int S = a.group_offset[b + 1] - s0;
+  const int s0 = group_off(a, b);
+  const int S = group_off(a, b + 1) - s0;
   // Whole workgroup: no split partials, or every row past this sequence's rows.
   if (S <= 1 || (int)(blockIdx.x % row_groups) * kCombineRows >= rows) return;
   const bool live = r < rows;
@@ -1328,8 +1350,8 @@ __global__ void __launch_bounds__(64 * kCombineSmallRows) mla_verify_combine_sma
   int node0, T;
   seq_tree(a, b, node0, T);
   const int rows = T * a.heads;
-  const int s0 = a.group_offset[b];
-  const int S = a.group_offset[b + 1] - s0;
+  const int s0 = group_off(a, b);
+  const int S = group_off(a, b + 1) - s0;
   const int r = (int)(blockIdx.x % row_groups) * kCombineSmallRows + (int)(threadIdx.x >> 6);
   if (S <= 1 || r >= rows) return;  // uniform over the wave
   const int lane = lane_id();
@@ -1396,9 +1418,7 @@ int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks,
 }
 
 int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream) {
-  int max_groups = 0;
-  for (int b = 0; b < a.batch; ++b) max_groups = std::max(max_groups, a.group_offset[b + 1] - a.group_offset[b]);
-  if (max_groups <= kCombineSmallMax) {
+  if (a.max_groups <= kCombineSmallMax) {
     const int64_t wgs = (int64_t)a.batch * ((a.max_rows_per_seq + kCombineSmallRows - 1) / kCombineSmallRows);
     if (wgs == 0) return 0;
     if (dtype == MLA_DTYPE_BF16)
@@ -1418,6 +1438,10 @@ int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream) {
     hipLaunchKernelGGL(mla_verify_combine_kernel<float>, dim3((unsigned)groups), dim3(kCombineThreads), 0,
                        (hipStream_t)stream, a);
   return (int)hipGetLastError();
+}
+
+int copy_tables_to_device(void* dst, const void* src, size_t bytes, void* stream) {
+  return (int)hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
 }
 
 // ===========================================================================

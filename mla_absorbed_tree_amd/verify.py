@@ -34,6 +34,12 @@ class MlaVerify:
             kv_c_row_stride, k_pe_row_stride, tree_len_host=tree_lens)
         self.info = B.mla_verify_plan_get_info(self.plan)
         self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=device)
+        # Batches above MLA_VERIFY_ARG_TABLE_BATCH read their per-sequence tables from device
+        # memory: staged once here, on the current stream, kept alive with the plan.
+        self.tables = None
+        if self.info["table_bytes"] > 0:
+            self.tables = torch.empty(self.info["table_bytes"] // 4, dtype=torch.int32, device=device)
+            B.mla_verify_plan_stage_tables(self.plan, self.tables)
 
     def __call__(self, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents, scale,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,

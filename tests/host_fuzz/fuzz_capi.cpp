@@ -3,6 +3,7 @@
 // tests/test_host_sanitizer.py. The kernel launchers are stubs that check the
 // argument block they receive (workspace regions inside the workspace, offset
 // tables consistent with the plan) instead of launching anything.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -38,17 +39,32 @@ uint64_t next() {
 }
 int64_t uni(int64_t lo, int64_t hi) { return lo + int64_t(next() % uint64_t(hi - lo + 1)); }
 
+// What the stubbed table copy received: the device address and the bytes.
+const void* g_tables_dev = nullptr;
+std::vector<int32_t> g_tables_host;
+
 void check_args(const mlav::VerifyArgs& a) {
   check(a.batch >= 1 && a.batch <= MLA_VERIFY_MAX_BATCH, "batch");
   check(reinterpret_cast<uintptr_t>(a.status) == g_ws, "status words at workspace offset 0");
+  // Tables in the arguments up to MLA_VERIFY_ARG_TABLE_BATCH, else the staged copy.
+  check((a.dev_tables != nullptr) == (a.batch > MLA_VERIFY_ARG_TABLE_BATCH), "table location");
+  if (a.dev_tables)
+    check(a.dev_tables == g_tables_dev && g_tables_host.size() == 3 * size_t(a.batch + 1), "staged tables");
+  auto tab = [&](int t, int i) {
+    if (a.dev_tables) return g_tables_host[size_t(t) * (a.batch + 1) + i];
+    return t == 0 ? a.split_offset[i] : t == 1 ? a.group_offset[i] : a.node_offset[i];
+  };
+  int max_groups = 0;
   for (int b = 0; b < a.batch; ++b) {
-    check(a.split_offset[b] <= a.split_offset[b + 1], "split offsets monotone");
-    check(a.group_offset[b] <= a.group_offset[b + 1], "group offsets monotone");
-    check(a.node_offset[b] <= a.node_offset[b + 1], "node offsets monotone");
+    check(tab(0, b) <= tab(0, b + 1), "split offsets monotone");
+    check(tab(1, b) <= tab(1, b + 1), "group offsets monotone");
+    check(tab(2, b) <= tab(2, b + 1), "node offsets monotone");
+    max_groups = std::max(max_groups, tab(1, b + 1) - tab(1, b));
   }
+  check(a.max_groups == max_groups, "max_groups");
   check(a.part_rows >= a.max_rows_per_seq, "partial rows cover every sequence");
   if (a.part_o) {
-    const size_t rows = size_t(a.group_offset[a.batch]) * size_t(a.part_rows);  // one per split group
+    const size_t rows = size_t(tab(1, a.batch)) * size_t(a.part_rows);  // one per split group
     const uintptr_t o = reinterpret_cast<uintptr_t>(a.part_o), ml = reinterpret_cast<uintptr_t>(a.part_ml);
     check(ml >= g_ws + 4 * size_t(a.batch), "partials after the status words");
     check(ml + rows * 8 <= o, "(m, l) before O");
@@ -80,6 +96,12 @@ int launch_kv_compact(const KvCompactArgs& a, int es, void*) {
   check(a.total > 0, "total");
   return 0;
 }
+int copy_tables_to_device(void* dst, const void* src, size_t bytes, void*) {
+  check(bytes % 4 == 0, "table bytes");
+  g_tables_dev = dst;
+  g_tables_host.assign(static_cast<const int32_t*>(src), static_cast<const int32_t*>(src) + bytes / 4);
+  return 0;
+}
 size_t noalloc_scratch_bytes() { return size_t(MLA_VERIFY_NOALLOC_WORKSPACE_BYTES); }
 int noalloc_scratch(void** ptr) {
   *ptr = reinterpret_cast<void*>(g_ws);
@@ -97,7 +119,7 @@ int main(int argc, char** argv) {
     const bool bad = uni(0, 4) == 0;
     auto pick = [&](int64_t lo, int64_t hi, int64_t blo, int64_t bhi) { return bad && uni(0, 5) == 0 ? uni(blo, bhi) : uni(lo, hi); };
     mla_verify_problem p{};
-    p.batch = int32_t(pick(1, uni(0, 3) ? 16 : 256, -2, 300));
+    p.batch = int32_t(pick(1, uni(0, 3) ? 16 : uni(0, 3) ? 256 : 1200, -2, MLA_VERIFY_MAX_BATCH + 2));
     p.num_heads = int32_t(pick(1, 130, -1, 0));
     p.tree_nodes = int32_t(pick(1, uni(0, 1) ? 64 : 256, -1, 300));
     p.d_latent = int32_t(pick(512, 512, 500, 520));
@@ -135,6 +157,17 @@ int main(int argc, char** argv) {
     void* ws = reinterpret_cast<void*>(g_ws);
     const int32_t* ip = static_cast<const int32_t*>(fake);
     float* fo = static_cast<float*>(fake);
+    // Batches above MLA_VERIFY_ARG_TABLE_BATCH run only once their tables are staged.
+    check(info.table_bytes == (p.batch > MLA_VERIFY_ARG_TABLE_BATCH ? 12 * size_t(p.batch + 1) : 0), "table bytes");
+    void* const tables = reinterpret_cast<void*>(uintptr_t(1) << 42);
+    if (info.table_bytes > 0) {
+      check(mla_verify_run(plan, fake, fake, fake, fake, ip, ip, ip, 0.07f, fo, fo, ws, ws_bytes, nullptr) ==
+                MLA_ERR_INVALID_ARG,
+            "run before the tables are staged");
+      check(mla_verify_plan_stage_tables(plan, tables, info.table_bytes - 4, nullptr) == MLA_ERR_INVALID_ARG,
+            "short table buffer");
+    }
+    check(mla_verify_plan_stage_tables(plan, tables, info.table_bytes, nullptr) == MLA_OK, "stage tables");
     const mla_status r = mla_verify_run(plan, fake, fake, fake, fake, ip, ip, ip, 0.07f, fo, fo, ws, ws_bytes, nullptr);
     check(r == MLA_OK, "run with valid arguments");
     check(mla_verify_run(plan, fake, fake, fake, fake, ip, ip, ip, 0.07f, fo, fo, ws, ws_bytes - 1, nullptr) ==

@@ -46,7 +46,7 @@ def test_status_strings(B):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(batch=0), -1), (dict(batch=257), -1), (dict(num_heads=0), -1),
+    (dict(batch=0), -1), (dict(batch=65537), -1), (dict(num_heads=0), -1),
     (dict(tree_nodes=0), -1), (dict(tree_nodes=257), -2), (dict(d_latent=256), -2),
     (dict(d_rope=32), -2), (dict(dtype=7), -1), (dict(kv_c_row_stride=500), -1),
     (dict(kv_c_row_stride=516), -1), (dict(k_pe_row_stride=60), -1), (dict(num_splits=-1), -1),
@@ -205,6 +205,29 @@ def test_plans_of_the_named_workloads(B):
             T = Tb if Tb is not None else np.full(cfg.batch, cfg.tree_nodes)
             assert info["partial_rows"] == (g * int(np.sum(T)) * cfg.heads if g > 1 else 0), name
             assert info["uses_combine"] == int(g > 1), name
+
+
+def test_large_batch_needs_staged_tables(B):
+    """Above MLA_VERIFY_ARG_TABLE_BATCH sequences a plan's tables go to device
+    memory: the plan reports their size, runs fail until they are staged, and
+    staging checks the buffer (all before any device work)."""
+    p, ws = B.mla_verify_plan(1000, 4, 8, 1, [100] * 1000)
+    info = B.mla_verify_plan_get_info(p)
+    assert info["table_bytes"] == 12 * 1001
+    fake = 1 << 20  # never dereferenced: the calls fail validation first
+    with pytest.raises(B.MlaVerifyError) as e:
+        B.mla_verify_run(p, fake, fake, fake, fake, fake, fake, fake, 0.1, fake, fake, 1 << 21, ws, stream=0)
+    assert e.value.status == B.MLA_ERR_INVALID_ARG and "mla_verify_plan_stage_tables" in str(e.value)
+    with pytest.raises(B.MlaVerifyError):
+        B.mla_verify_plan_stage_tables(p, fake, info["table_bytes"] - 4, stream=0)
+    with pytest.raises(B.MlaVerifyError):
+        B.mla_verify_plan_stage_tables(p, fake + 2, info["table_bytes"], stream=0)
+    B.mla_verify_plan_destroy(p)
+    # at the argument-table bound nothing is staged and staging is a no-op
+    p, _ = B.mla_verify_plan(B.MLA_VERIFY_ARG_TABLE_BATCH, 4, 8, 1, [100] * B.MLA_VERIFY_ARG_TABLE_BATCH)
+    assert B.mla_verify_plan_get_info(p)["table_bytes"] == 0
+    B.mla_verify_plan_stage_tables(p, None, 0, stream=0)
+    B.mla_verify_plan_destroy(p)
 
 
 def test_varlen_run_requires_tree_indptr(B):

@@ -176,12 +176,78 @@ def test_ragged_long_prefixes_sampled():
 
 @pytest.mark.parametrize("dtype,splits", [("bf16", 0), ("bf16", 3), ("f32", 0)])
 def test_max_batch(dtype, splits):
-    """256 sequences (the batch limit): every offset table of the launch at full
-    length; tree sizes 0..9 and prefixes 0..300, all rows against the oracle."""
+    """256 sequences (the largest batch whose tables travel in the launch
+    arguments): every offset table of the launch at full length; tree sizes
+    0..9 and prefixes 0..300, all rows against the oracle."""
     cfg = get_config("b8_h64_paged600k_t16_bf16", batch=256, heads=4, tree_nodes=9,
                      tree_range=(0, 9), prefix_range=(0, 300), pool_slots=45000, dtype=dtype,
                      seed=50)
     _full(cfg, splits, poison_unused=True)
+
+
+@pytest.mark.parametrize("dtype,splits", [("bf16", 0), ("bf16", 3), ("f32", 3)])
+def test_batch_beyond_the_argument_tables(dtype, splits):
+    """1100 sequences: above MLA_VERIFY_ARG_TABLE_BATCH the per-sequence
+    tables live in device memory staged once by mla_verify_plan_stage_tables
+    (MlaVerify does it). Tree sizes 0..9 and prefixes 0..300, all rows against
+    the oracle; then one run captured in a graph and replayed, bitwise equal
+    to the eager run, and the status words of all sequences (one bad tree)."""
+    import torch
+    from mla_absorbed_tree_amd import binding as B
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+    cfg = get_config("b8_h64_paged600k_t16_bf16", batch=1100, heads=4, tree_nodes=9,
+                     tree_range=(0, 9), prefix_range=(0, 300), pool_slots=400000, dtype=dtype,
+                     seed=52)
+    x = make_inputs(cfg, poison_unused=True)
+    bad_seq = int(np.flatnonzero(np.asarray(x.tree_lens) >= 3)[-1])   # a sequence with >= 3 nodes
+    n0, n1 = int(x.tree_indptr[bad_seq]), int(x.tree_indptr[bad_seq + 1])
+    good_parent = int(x.parents[n0 + 2])
+    x.parents[n0 + 2] = 2                                               # node 2 names itself: invalid
+    d = device_inputs(x)
+    # rows of node 2 of that tree and of its descendants are NaN
+    bad_nodes = {2}
+    for t in range(3, n1 - n0):
+        if int(x.parents[n0 + t]) in bad_nodes:
+            bad_nodes.add(t)
+    good = np.ones(int(x.tree_indptr[-1]), dtype=bool)
+    good[[n0 + t for t in bad_nodes]] = False
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, dtype, x.kv_lens, splits, tree_lens=x.tree_lens)
+    assert mv.info["table_bytes"] == 12 * (cfg.batch + 1) and mv.tables is not None, mv.info
+    args = (d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"], d["kv_indices"], d["tree_parents"])
+    o, lse = mv(*args, x.scale)
+    torch.cuda.synchronize()
+    log("case %s splits=%d plan=%s" % (cfg.name, splits, mv.info))
+    if dtype == "f32":  # one partial per split: the combine reads the staged group table too
+        assert mv.info["uses_combine"] == 1, mv.info
+    status = mv.workspace[:4 * cfg.batch].view(torch.int32).cpu().numpy()
+    want = np.zeros(cfg.batch, dtype=np.int32)
+    want[bad_seq] = B.MLA_VERIFY_STATUS_BAD_PARENT
+    np.testing.assert_array_equal(status, want)
+    o_np, lse_np = o.cpu().numpy(), lse.cpu().numpy()
+    assert np.isnan(o_np[~good]).all() and np.isnan(lse_np[~good]).all()
+    x.parents[n0 + 2] = good_parent  # the oracle rejects invalid trees; valid rows match anyway
+    o_ref, lse_ref = run_oracle(x)
+    compare(o_np[good], lse_np[good], o_ref[good], lse_ref[good], dtype)
+    good_t = torch.from_numpy(good).cuda()
+
+    out = torch.empty_like(o)
+    lse2 = torch.empty_like(lse)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the capture stream
+        mv(*args, x.scale, out=out, lse=lse2)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mv(*args, x.scale, out=out, lse=lse2)
+    for rep in range(2):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out[good_t], o[good_t]) and torch.equal(lse2[good_t], lse[good_t]), rep
+    mv.close()
 
 
 def test_ragged_bench_workload_sampled():

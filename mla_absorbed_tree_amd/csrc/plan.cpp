@@ -24,7 +24,7 @@ std::string fmt(const char* f, long long a = 0, long long b = 0) {
 // plus a fixed start-up (Q and tree loads, pipeline fill, epilogue). Split
 // partials add their write and the combine's read at HBM speed.
 constexpr double kWgOverheadTiles = 4.0;
-constexpr double kTileSeconds = 1.85e-6;      // one tile of one 128-row workgroup (measured)
+constexpr double kTileSeconds = 1.75e-6;      // one tile of one 128-row workgroup (measured)
 constexpr double kHbmBytesPerSecond = 5.0e12; // sustained partial write/read rate
 
 double estimate_launch(const std::vector<int64_t>& tiles, const std::vector<int64_t>& row_blocks,

@@ -247,6 +247,11 @@ def test_batch_beyond_the_argument_tables(dtype, splits):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out[good_t], o[good_t]) and torch.equal(lse2[good_t], lse[good_t]), rep
+    # the same trees read on the device (mla_verify_run_varlen) through the staged node table
+    out.fill_(float("nan"))
+    B.mla_verify_run_varlen(mv.plan, *args[:6], _dev(x.tree_indptr), args[6], x.scale, out, lse2, mv.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(out[good_t], o[good_t]) and torch.equal(lse2[good_t], lse[good_t])
     mv.close()
 
 

@@ -234,6 +234,8 @@ mla_status mla_verify_run_varlen(mla_verify_plan_t plan, const void* q_nope, con
  * calls that overlap on one GPU race: calls on one stream are ordered, calls on
  * different streams or threads must be ordered by the caller.  The status words
  * of these calls are not readable by the caller (use mla_verify_run for them).
+ * A plan of more than MLA_VERIFY_ARG_TABLE_BATCH sequences still needs its
+ * tables staged (mla_verify_plan_stage_tables, once, in caller memory).
  */
 #define MLA_VERIFY_NOALLOC_WORKSPACE_BYTES (64u << 20)
 mla_status mla_verify_run_noalloc(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,

@@ -266,6 +266,38 @@ def test_split_invariance_at_full_size():
         assert np.abs(l - l1).max() < 1e-4
 
 
+@pytest.mark.parametrize("name,splits,combine", [("b1_h64_p4096_t16_bf16", 1, "none"),
+                                                ("b1_h64_p4096_t16_bf16", 4, "one wave per row"),
+                                                ("b1_h64_p4096_t16_bf16", 40, "lane groups"),
+                                                ("tiny_f32_b1_h16_p256_t8", 3, "one wave per row")])
+def test_attend_then_combine_equals_run(name, splits, combine):
+    """mla_verify_attend followed by mla_verify_combine on one stream is
+    mla_verify_run, bit for bit: without a combine, and through both combine
+    kernels (up to 8 split groups per row one wave per row, else lane groups)."""
+    import torch
+    from mla_absorbed_tree_amd import binding as B
+    from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
+    cfg = get_config(name, heads=8 if name.startswith("b1") else 16)
+    x = make_inputs(cfg)
+    d = device_inputs(x)
+    mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, splits)
+    groups = mv.info["total_groups"] // cfg.batch
+    assert (combine == "none") == (groups == 1) and (combine == "lane groups") == (groups > 8), mv.info
+    args = (d["q_nope"], d["q_pe"], d["kv_c"], d["k_pe"], d["kv_indptr"], d["kv_indices"], d["tree_parents"],
+            x.scale)
+    o1, l1 = mv(*args)
+    o2 = torch.full_like(o1, float("nan"))
+    l2 = torch.full_like(l1, float("nan"))
+    B.mla_verify_attend(mv.plan, *args, o2, l2, mv.workspace)
+    B.mla_verify_combine(mv.plan, o2, l2, mv.workspace)
+    torch.cuda.synchronize()
+    mv.close()
+    log("  %s splits=%d groups=%d (%s)" % (name, splits, groups, combine))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, lse_ref = run_oracle(x)
+    compare(o1.cpu().numpy(), l1.cpu().numpy(), o_ref, lse_ref, cfg.dtype)
+
+
 def test_repeat_runs_are_bitwise_identical():
     cfg = get_config("b1_h64_p4096_t16_bf16")
     x = make_inputs(cfg)

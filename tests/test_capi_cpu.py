@@ -166,7 +166,8 @@ def test_ragged_tree_plans(B):
 def test_planning_large_batches_is_fast(B):
     """The automatic split search stays cheap for big batches of long sequences."""
     import time
-    for b, h, t, n in ((256, 64, 64, 200000), (256, 1, 1, 200000), (1, 64, 256, 200256)):
+    for b, h, t, n in ((256, 64, 64, 200000), (256, 1, 1, 200000), (1, 64, 256, 200256),
+                       (B.MLA_VERIFY_MAX_BATCH, 8, 4, 40000)):
         t0 = time.perf_counter()
         p, _ = B.mla_verify_plan(b, h, t, 1, [n] * b)
         assert time.perf_counter() - t0 < 0.5, (b, h, t, n)

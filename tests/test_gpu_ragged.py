@@ -255,6 +255,17 @@ def test_batch_beyond_the_argument_tables(dtype, splits):
     mv.close()
 
 
+def test_largest_batch():
+    """MLA_VERIFY_MAX_BATCH sequences of one- or two-node trees with prefixes of
+    0..12 keys in a paged pool (decode-like steps at the largest batch): one
+    workgroup per sequence, tables staged to the device; all rows against the
+    oracle."""
+    from mla_absorbed_tree_amd import binding as B
+    cfg = get_config("b8_h64_paged600k_t16_bf16", batch=B.MLA_VERIFY_MAX_BATCH, heads=2, tree_nodes=2,
+                     tree_range=(1, 2), prefix_range=(0, 12), pool_slots=520000, seed=53)
+    _full(cfg, 0)
+
+
 def test_ragged_bench_workload_sampled():
     """The benchmark's packed-tree workload at full size and in its launch
     configuration (automatic splits): sampled nodes, on both sides of the

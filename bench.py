@@ -132,10 +132,10 @@ def bench_workload(name, steps, warmup, num_splits=None):
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     achieved = flops / (attn_ms * 1e-3)
     # Split partials: each (group, row) partial is written by the attention
-    # launch and read back by the combine: (m, l) in fp32 and O in the problem
-    # dtype.
+    # launch and read back by the combine: an fp32 (m, l, s0, s1) record and
+    # O (scaled fp16 for bf16 problems, fp32 for fp32 problems).
     part_elem = 2 if cfg.dtype == "bf16" else 4
-    partial_bytes = 2 * int(mv.info["partial_rows"]) * (2 * 4 + 512 * part_elem)
+    partial_bytes = 2 * int(mv.info["partial_rows"]) * (4 * 4 + 512 * part_elem)
     res = {
         "workload": name,
         "value": kv_tokens / (step_ms * 1e-3),

@@ -251,10 +251,12 @@ mla_status mla_verify_run_noalloc(mla_verify_plan_t plan, const void* q_nope, co
  * one reference max, so their merge is a plain sum kept in the workgroup's
  * accumulators. Sequences with a single split group write out/lse directly;
  * the others leave one partial per split group in the workspace: (m, l) in
- * fp32, and the group's unnormalised output O = l * o_group in the problem
- * dtype (fp32 for fp32 problems; bf16 for bf16 problems, whose rounding,
- * <= 2^-9 relative per element, moves the result by <= 2^-9 max |o_group|,
- * far below the bf16 tolerance).
+ * fp32, and the group's unnormalised output O = l * o_group: fp32 for fp32
+ * problems; for bf16 problems fp16 times a power of two per row and feature
+ * half (kept in the row's fp32 record), which moves the result by at most
+ * 2^-12 of that half's largest |o_group| (bf16 storage would move each
+ * element by up to 2^-9 of itself, about 8e-3 where a row's weight sits on
+ * a few keys with latent values near 4).
  * mla_verify_combine then merges those partials by log-sum-exp into out/lse
  * (it enqueues nothing when no sequence has more than one split group,
  * uses_combine = 0). Calling attend and

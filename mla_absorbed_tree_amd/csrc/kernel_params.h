@@ -26,10 +26,11 @@ struct VerifyArgs {
   float* lse;                  // [nodes, H] or nullptr
   // Partials, one per split group [total_groups, part_rows, 512] (when some
   // sequence has several groups; group_offset[b] is sequence b's first):
-  // unnormalised O = sum of 2^(s - m) v, fp32 for fp32 problems, bf16 for
-  // bf16 problems. Rows past a sequence's T_b * H are padding (never read).
+  // unnormalised O = sum of 2^(s - m) v, fp32 for fp32 problems; for bf16
+  // problems fp16, feature half f scaled by 1 / s_f of the row's record.
+  // Rows past a sequence's T_b * H are padding (never read).
   void* part_o;
-  float* part_ml;              // [total_groups, part_rows, 2]  (m in log2 units, l)
+  float* part_ml;              // [total_groups, part_rows, 4]  (m in log2 units, l, s_0, s_1)
   int32_t* status;             // [batch] per-sequence status words (MLA_VERIFY_STATUS_*)
   int64_t kv_c_stride;         // elements
   int64_t k_pe_stride;         // elements

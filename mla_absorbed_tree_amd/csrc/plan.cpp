@@ -268,7 +268,7 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
     // kernel stores unconditionally, padding rows included).
     const size_t part_rows = size_t(plan.total_groups) * size_t(plan.row_blocks) * size_t(plan.rows_per_block);
     plan.ws_part_ml = off;
-    off = align_up(off + part_rows * 2 * sizeof(float), 256);
+    off = align_up(off + part_rows * 4 * sizeof(float), 256);
     plan.ws_part_o = off;
     const size_t part_elem = p.dtype == MLA_DTYPE_BF16 ? 2 : sizeof(float);
     off = align_up(off + part_rows * kDl * part_elem, 256);

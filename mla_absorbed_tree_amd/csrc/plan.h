@@ -46,8 +46,8 @@ struct Plan {
   // Workspace layout (byte offsets from the workspace start).
   size_t ws_status = 0;         // int32 [batch] status words (MLA_VERIFY_STATUS_*)
   // Per (split group, row), rows padded to row_blocks * rows_per_block per group:
-  size_t ws_part_ml = 0;        // float2 (m in log2 units, l)
-  size_t ws_part_o = 0;         // [512] unnormalised O: fp32, or bf16 for bf16 problems
+  size_t ws_part_ml = 0;        // float4 (m in log2 units, l, s_0, s_1)
+  size_t ws_part_o = 0;         // [512] unnormalised O: fp32, or scaled fp16 for bf16 problems
   size_t ws_bytes = 0;
 };
 

@@ -53,16 +53,17 @@
 namespace mlav {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Two floats rounded to bf16 (nearest even), the first in the low half.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
+// Two floats rounded to fp16 (nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
 }
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -751,11 +752,19 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
 
   // Partial c of the sequence's split groups (sequences with several
   // groups): (m, l) of this wave's rows (both lanes of a row hold the same
-  // values), written by this wave, and the raw O in bf16 (half the bytes of
-  // fp32; the rounding is relative to each partial and averages out in the
-  // merge), of which this wave holds feature half fhalf of its own and its
-  // partner's rows. Nothing is exchanged, so no barrier. Accumulator register
-  // i of block fb holds feature 256*fhalf + 32fb + (i/4)*8 + 4*half + i%4.
+  // values), written by this wave, and the raw O of feature half fhalf of its
+  // own and its partner's rows. Nothing is exchanged, so no barrier.
+  // Accumulator register i of block fb holds feature 256*fhalf + 32fb +
+  // (i/4)*8 + 4*half + i%4.
+  //
+  // O goes out in fp16 times a power of two per (row, feature half), 2^(15 -
+  // e) where 2^e bounds the half's largest |O|, and that power's inverse goes
+  // to the row's (m, l) record. The result moves by at most 2^-12 of the
+  // feature half's largest |o|, where bf16's 8 significant bits would move
+  // each element by up to 2^-9 of itself: about 8e-3 on rows whose weight
+  // sits on a few keys with latent values near 4. The bytes are those of
+  // bf16, half those of fp32: at a long prefix every workgroup ends at once,
+  // and nothing hides this store burst.
   //
   // The partial arrays have a.part_rows (a multiple of kRows) rows per
   // group, so the rows past T_b * H of the last row block have room and every
@@ -770,11 +779,27 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
     const bool node_ok = row_valid(wave);
     mfma_result_wait();  // the last PV MFMAs may have just been issued
     const int64_t prow0 = (int64_t)c * a.part_rows + w.rb * kRows + qcol;
-    *(float2*)(a.part_ml + 2 * (prow0 + wave * 32)) = make_float2(node_ok ? m_ref : NAN, node_ok ? l_tot : NAN);
+    *(float2*)(a.part_ml + 4 * (prow0 + wave * 32)) = make_float2(node_ok ? m_ref : NAN, node_ok ? l_tot : NAN);
 #pragma unroll
     for (int rbk = 0; rbk < 2; ++rbk) {
       const int64_t prow = prow0 + (rbk ? partner : wave) * 32;
-      __bf16* dst = (__bf16*)a.part_o + prow * kDl + fhalf * 256 + 8 * half;
+      // Largest |O| of the row's feature half (128 values in each wave half).
+      float mx = 0.f;
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const f32x4_t t = read_acc4(oacc[rbk][fb], gi);
+          mx = fmaxf(mx, fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3]))));
+        }
+      mx = fmaxf(mx, swap_halves(mx));
+      // mx = f * 2^e with f in [0.5, 1), so |O| * 2^(15 - e) < 2^15, inside
+      // fp16's range however large O is; e is held at -100 or above so that
+      // both powers stay normal floats.
+      const int e = max(__builtin_amdgcn_frexp_expf(mx), -100);
+      const float down = __builtin_amdgcn_ldexpf(1.f, 15 - e);
+      if (half == 0) a.part_ml[4 * prow + 2 + fhalf] = __builtin_amdgcn_ldexpf(1.f, e - 15);
+      _Float16* dst = (_Float16*)a.part_o + prow * kDl + fhalf * 256 + 8 * half;
 #pragma unroll
       for (int fb = 0; fb < 8; ++fb)
 #pragma unroll
@@ -783,16 +808,16 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
           // 4*half + 0..3 of the block) become 8 consecutive features per
           // lane by one exchange between the wave halves: the lower half
           // keeps 16m..16m+7, the upper half gets 16m+8..16m+15.
-          const f32x4_t t0 = read_acc4(oacc[rbk][fb], 2 * m);
-          const f32x4_t t1 = read_acc4(oacc[rbk][fb], 2 * m + 1);
+          const f32x4_t t0 = read_acc4(oacc[rbk][fb], 2 * m) * down;
+          const f32x4_t t1 = read_acc4(oacc[rbk][fb], 2 * m + 1) * down;
           uint32_t x[2], y[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            x[e] = pack_bf16x2(t0[2 * e], t0[2 * e + 1]);
-            y[e] = pack_bf16x2(t1[2 * e], t1[2 * e + 1]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
-            x[e] = sw[0];
-            y[e] = sw[1];
+          for (int k = 0; k < 2; ++k) {
+            x[k] = pack_f16x2(t0[2 * k], t0[2 * k + 1]);
+            y[k] = pack_f16x2(t1[2 * k], t1[2 * k + 1]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(x[k], y[k], false, false);
+            x[k] = sw[0];
+            y[k] = sw[1];
           }
           *(u32x4_t*)(dst + 32 * fb + 16 * m) = u32x4_t{x[0], x[1], y[0], y[1]};
           // One pair at a time: otherwise the scheduler reads every
@@ -1198,8 +1223,8 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
     dst = (float*)a.part_o + prow * kDl;
     mul = 1.f;
     if (half == 0) {
-      a.part_ml[2 * prow] = node_ok ? m_ref : NAN;
-      a.part_ml[2 * prow + 1] = node_ok ? l_tot : NAN;
+      a.part_ml[4 * prow] = node_ok ? m_ref : NAN;
+      a.part_ml[4 * prow + 1] = node_ok ? l_tot : NAN;
     }
   }
 #pragma unroll
@@ -1218,12 +1243,14 @@ mla_verify_attn_f32_kernel(const VerifyArgs a) {
 // ===========================================================================
 // Merge the partials (one per split group) of kCombineRows consecutive query
 // rows of one sequence: M = max m_c, w_c = 2^(m_c - M), L = sum w_c l_c,
-// out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Partials O_c are fp32 (fp32
-// problems) or bf16 (bf16 problems). Each row has 4 lane groups of 32 lanes
-// (16 features per lane); lane group g sums the partials c = g (mod 4), and
-// their sums meet in LDS. The rows of a workgroup are adjacent in every
-// partial block. Empty partials (m = -inf, or l = 0 and O = 0) get weight 0;
-// a NaN partial (invalid tree) makes the row NaN.
+// out = sum w_c O_c / L, lse = (M + log2 L) ln 2. Each partial row is a
+// record (m, l, s_0, s_1) and its O_c: fp32 for fp32 problems (s unused),
+// fp16 for bf16 problems, where feature half f of O_c is the stored value
+// times s_f. Each row has 4 lane groups of 32 lanes (16 features per lane);
+// lane group g sums the partials c = g (mod 4), and their sums meet in LDS.
+// The rows of a workgroup are adjacent in every partial block. Empty
+// partials (m = -inf, or l = 0 and O = 0) get weight 0; a NaN partial
+// (invalid tree) makes the row NaN.
 constexpr int kCombineRows = 2;
 constexpr int kCombineGroups = 4;
 constexpr int kCombineThreads = 32 * kCombineGroups * kCombineRows;
@@ -1231,9 +1258,8 @@ constexpr int kCombineStage = 256;
 
 template <typename PartT>
 __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(const VerifyArgs a) {
-  constexpr bool kBf16 = sizeof(PartT) == 2;
-  __shared__ float wsh[kCombineRows][kCombineStage];
-  __shared__ float lsh[kCombineRows][kCombineGroups];
+  constexpr bool kF16 = sizeof(PartT) == 2;
+  __shared__ float wsh[kCombineRows][kCombineStage][2];
   __shared__ f32x4_t accsh[kCombineRows][kCombineGroups - 1][32][4];
   const int row_groups = (a.max_rows_per_seq + kCombineRows - 1) / kCombineRows;
   const int b = (int)(blockIdx.x / row_groups);
@@ -1249,8 +1275,8 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   if (S <= 1 || (int)(blockIdx.x % row_groups) * kCombineRows >= rows) return;
   const bool live = r < rows;
   const int rr = live ? r : rows - 1;
-  const float* ml = a.part_ml + 2 * ((int64_t)s0 * a.part_rows + rr);
-  const int64_t ml_stride = 2 * (int64_t)a.part_rows;
+  const float* ml = a.part_ml + 4 * ((int64_t)s0 * a.part_rows + rr);
+  const int64_t ml_stride = 4 * (int64_t)a.part_rows;
 
   // Row max and NaN flag over the splits (every group computes it).
   float M = -INFINITY;
@@ -1267,22 +1293,22 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
 
   f32x4_t acc[4] = {};
   float lloc = 0.f;
-  // Lane t32 of a group holds 16 of the row's 512 features: for bf16 the
-  // 8-feature runs starting at 8*t32 and 256 + 8*t32, for fp32 the 4-feature
-  // runs at 4*t32 + 128*q, so that each load instruction of a group reads
-  // 512 contiguous bytes.
-  const PartT* po = (const PartT*)a.part_o + ((int64_t)s0 * a.part_rows + rr) * kDl + (kBf16 ? 8 : 4) * t32;
+  // Lane t32 of a group holds 16 of the row's 512 features: for fp16 the
+  // 8-feature runs starting at 8*t32 (feature half 0) and 256 + 8*t32
+  // (feature half 1), for fp32 the 4-feature runs at 4*t32 + 128*q, so that
+  // each load instruction of a group reads contiguous bytes.
+  const PartT* po = (const PartT*)a.part_o + ((int64_t)s0 * a.part_rows + rr) * kDl + (kF16 ? 8 : 4) * t32;
   const int64_t po_stride = (int64_t)a.part_rows * kDl;
   for (int base = 0; base < S; base += kCombineStage) {
     const int cnt = min(kCombineStage, S - base);
     __syncthreads();
     if (grp == 0) {
       for (int cc = t32; cc < cnt; cc += 32) {
-        const float m = ml[(base + cc) * ml_stride];
-        const float l = ml[(base + cc) * ml_stride + 1];
-        const float wgt = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-        wsh[j][cc] = wgt;
-        lloc += wgt * l;
+        const f32x4_t rec = *(const f32x4_t*)(ml + (base + cc) * ml_stride);
+        const float wgt = rec[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rec[0] - M);
+        wsh[j][cc][0] = kF16 ? wgt * rec[2] : wgt;
+        wsh[j][cc][1] = kF16 ? wgt * rec[3] : wgt;
+        lloc += wgt * rec[1];
       }
     }
     __syncthreads();
@@ -1290,12 +1316,12 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
     // so that several are in flight at once.
 #pragma unroll 4
     for (int cc = grp; cc < cnt; cc += kCombineGroups) {
-      const float wgt = wsh[j][cc];
       const PartT* src = po + (base + cc) * po_stride;
-      if constexpr (kBf16) {
+      if constexpr (kF16) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const bf16x8_t v = *(const bf16x8_t*)(src + 256 * q);
+          const float wgt = wsh[j][cc][q];
+          const f16x8_t v = *(const f16x8_t*)(src + 256 * q);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             acc[2 * q][e] += wgt * (float)v[e];
@@ -1303,6 +1329,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
           }
         }
       } else {
+        const float wgt = wsh[j][cc][0];
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[q] += wgt * *(const f32x4_t*)(src + 128 * q);
       }
@@ -1324,27 +1351,28 @@ __global__ void __launch_bounds__(kCombineThreads) mla_verify_combine_kernel(con
   const float inv = nan ? NAN : 1.f / lloc;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    // acc[q]: features 8*t32 + 256*(q/2) + 4*(q%2) (bf16) or 4*t32 + 128*q (fp32).
-    const int f = kBf16 ? 8 * t32 + 256 * (q >> 1) + 4 * (q & 1) : 4 * t32 + 128 * q;
+    // acc[q]: features 8*t32 + 256*(q/2) + 4*(q%2) (fp16) or 4*t32 + 128*q (fp32).
+    const int f = kF16 ? 8 * t32 + 256 * (q >> 1) + 4 * (q & 1) : 4 * t32 + 128 * q;
     *(f32x4_t*)(a.out + grow * kDl + f) = acc[q] * inv;
   }
   if (t32 == 0 && a.lse) a.lse[grow] = nan ? NAN : (M + __log2f(lloc)) * kLn2;
 }
 
 // The same merge when no sequence has more than kCombineSmallMax split
-// groups, one wave per row and no LDS: lane l holds features 8l..8l+7, so
-// each partial is one 16-byte (bf16) or 32-byte (fp32) load per lane and the
-// wave reads it as one contiguous block; every lane reads the row's (m, l)
-// pairs itself (the same addresses across the wave). Measured against the
-// kernel above: 20 -> 9 us at 2 groups per row (32k prefix, 16k rows); at 16
-// groups per row and 2k rows (200k prefix) one wave per row has too little
-// parallelism and ran about 5 us slower, hence the bound of 8.
+// groups, one wave per row and no LDS: lane l holds features 8l..8l+7 (of
+// feature half l/32), so each partial is one 16-byte (fp16) or 32-byte
+// (fp32) load per lane and the wave reads it as one contiguous block; every
+// lane reads the row's (m, l, s_0, s_1) records itself (the same addresses
+// across the wave). Measured against the kernel above: 20 -> 9 us at 2
+// groups per row (32k prefix, 16k rows); at 16 groups per row and 2k rows
+// (200k prefix) one wave per row has too little parallelism and ran about
+// 5 us slower, hence the bound of 8.
 constexpr int kCombineSmallMax = 8;
 constexpr int kCombineSmallRows = 4;  // waves (rows) per workgroup
 
 template <typename PartT>
 __global__ void __launch_bounds__(64 * kCombineSmallRows) mla_verify_combine_small_kernel(const VerifyArgs a) {
-  constexpr bool kBf16 = sizeof(PartT) == 2;
+  constexpr bool kF16 = sizeof(PartT) == 2;
   const int row_groups = (a.max_rows_per_seq + kCombineSmallRows - 1) / kCombineSmallRows;
   const int b = (int)(blockIdx.x / row_groups);
   int node0, T;
@@ -1355,19 +1383,20 @@ __global__ void __launch_bounds__(64 * kCombineSmallRows) mla_verify_combine_sma
   const int r = (int)(blockIdx.x % row_groups) * kCombineSmallRows + (int)(threadIdx.x >> 6);
   if (S <= 1 || r >= rows) return;  // uniform over the wave
   const int lane = lane_id();
-  const float* ml = a.part_ml + 2 * ((int64_t)s0 * a.part_rows + r);
-  const int64_t ml_stride = 2 * (int64_t)a.part_rows;
-  float m[kCombineSmallMax], l[kCombineSmallMax];
+  const float* ml = a.part_ml + 4 * ((int64_t)s0 * a.part_rows + r);
+  const int64_t ml_stride = 4 * (int64_t)a.part_rows;
+  float m[kCombineSmallMax], l[kCombineSmallMax], sc[kCombineSmallMax];
   float M = -INFINITY;
   bool nan = false;
 #pragma unroll
   for (int c = 0; c < kCombineSmallMax; ++c) {
     if (c < S) {
-      const float2 v = *(const float2*)(ml + c * ml_stride);
-      m[c] = v.x;
-      l[c] = v.y;
-      nan |= v.x != v.x;
-      M = fmaxf(M, v.x);
+      const f32x4_t v = *(const f32x4_t*)(ml + c * ml_stride);
+      m[c] = v[0];
+      l[c] = v[1];
+      sc[c] = lane < 32 ? v[2] : v[3];
+      nan |= v[0] != v[0];
+      M = fmaxf(M, v[0]);
     }
   }
   float L = 0.f;
@@ -1381,12 +1410,13 @@ __global__ void __launch_bounds__(64 * kCombineSmallRows) mla_verify_combine_sma
       const float wgt = m[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[c] - M);
       L += wgt * l[c];
       const PartT* src = po + c * po_stride;
-      if constexpr (kBf16) {
-        const bf16x8_t v = *(const bf16x8_t*)src;
+      if constexpr (kF16) {
+        const float ws = wgt * sc[c];
+        const f16x8_t v = *(const f16x8_t*)src;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[0][e] += wgt * (float)v[e];
-          acc[1][e] += wgt * (float)v[4 + e];
+          acc[0][e] += ws * (float)v[e];
+          acc[1][e] += ws * (float)v[4 + e];
         }
       } else {
         acc[0] += wgt * *(const f32x4_t*)src;
@@ -1418,12 +1448,13 @@ int launch_verify_attention(const VerifyArgs& a, int dtype, int64_t grid_blocks,
 }
 
 int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream) {
+  // Partials are fp16 (with scales) for bf16 problems, fp32 for fp32 problems.
   if (a.max_groups <= kCombineSmallMax) {
     const int64_t wgs = (int64_t)a.batch * ((a.max_rows_per_seq + kCombineSmallRows - 1) / kCombineSmallRows);
     if (wgs == 0) return 0;
     if (dtype == MLA_DTYPE_BF16)
-      hipLaunchKernelGGL(mla_verify_combine_small_kernel<__bf16>, dim3((unsigned)wgs), dim3(64 * kCombineSmallRows),
-                         0, (hipStream_t)stream, a);
+      hipLaunchKernelGGL(mla_verify_combine_small_kernel<_Float16>, dim3((unsigned)wgs),
+                         dim3(64 * kCombineSmallRows), 0, (hipStream_t)stream, a);
     else
       hipLaunchKernelGGL(mla_verify_combine_small_kernel<float>, dim3((unsigned)wgs), dim3(64 * kCombineSmallRows),
                          0, (hipStream_t)stream, a);
@@ -1432,7 +1463,7 @@ int launch_verify_combine(const VerifyArgs& a, int dtype, void* stream) {
   const int64_t groups = (int64_t)a.batch * ((a.max_rows_per_seq + kCombineRows - 1) / kCombineRows);
   if (groups == 0) return 0;
   if (dtype == MLA_DTYPE_BF16)
-    hipLaunchKernelGGL(mla_verify_combine_kernel<__bf16>, dim3((unsigned)groups), dim3(kCombineThreads), 0,
+    hipLaunchKernelGGL(mla_verify_combine_kernel<_Float16>, dim3((unsigned)groups), dim3(kCombineThreads), 0,
                        (hipStream_t)stream, a);
   else
     hipLaunchKernelGGL(mla_verify_combine_kernel<float>, dim3((unsigned)groups), dim3(kCombineThreads), 0,

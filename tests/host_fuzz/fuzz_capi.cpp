@@ -67,8 +67,8 @@ void check_args(const mlav::VerifyArgs& a) {
     const size_t rows = size_t(tab(1, a.batch)) * size_t(a.part_rows);  // one per split group
     const uintptr_t o = reinterpret_cast<uintptr_t>(a.part_o), ml = reinterpret_cast<uintptr_t>(a.part_ml);
     check(ml >= g_ws + 4 * size_t(a.batch), "partials after the status words");
-    check(ml + rows * 8 <= o, "(m, l) before O");
-    check(o + rows * 512 * 2 <= g_ws + g_ws_bytes, "O inside the workspace");  // bf16 lower bound
+    check(ml + rows * 16 <= o, "(m, l, s0, s1) before O");
+    check(o + rows * 512 * 2 <= g_ws + g_ws_bytes, "O inside the workspace");  // fp16 lower bound
   }
 }
 

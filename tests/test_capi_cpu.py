@@ -73,8 +73,9 @@ def test_forced_and_auto_split_schedules(B):
     assert info["splits_per_workgroup"] == 16
     assert info["grid_blocks"] == 256 // 16 * (rows // info["rows_per_block"])
     # one partial per workgroup's group of 16 splits (their merge is a sum
-    # in the accumulators): per (group, row) fp32 (m, l) and the bf16 output
-    assert 16 * rows * (2 * 4 + 512 * 2) <= ws < 17 * rows * (2 * 4 + 512 * 2)
+    # in the accumulators): per (group, row) an fp32 (m, l, s0, s1) record
+    # and the output in scaled fp16
+    assert 16 * rows * (4 * 4 + 512 * 2) <= ws < 17 * rows * (4 * 4 + 512 * 2)
     B.mla_verify_plan_destroy(p)
     # groups that do not divide the split counts: 3 splits per workgroup,
     # ceil(40/3) + ceil(32/3) + ceil(40/3) = 14 + 11 + 14 groups, padded to 8 XCDs

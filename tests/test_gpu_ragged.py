@@ -466,3 +466,35 @@ def test_random_shapes_sweep():
         o, lse, info = run_hip(x, splits)
         o_ref, lse_ref = run_oracle(x)
         compare(o, lse, o_ref, lse_ref, dtype, "plan=%s" % info)
+
+
+@pytest.mark.parametrize("kv_scale", [1.0, 1e4, 1e-6])
+@pytest.mark.parametrize("shape", ["few_keys", "peaked"])
+def test_split_partials_of_latent_size(shape, kv_scale):
+    """Split runs whose outputs are as large as a latent row (|o| up to about 4).
+
+    few_keys: no prefix, so a row sees only its ancestors (a handful of keys in
+    a uniform tree); 3 forced splits give 2..3 split groups per row, merged by
+    the one-wave-per-row combine. peaked: prefixes of 700 and 2000 keys with
+    queries 4x the usual size, so each row's softmax sits on a few keys; 40
+    forced splits give up to 40 groups per row, merged by the lane-group
+    combine. Either way each group's partial is of a latent row's size, where
+    storing the partials in bf16 (2^-9 of each element) put the result past
+    the bf16 bound (1.75e-2 measured on the few_keys kind). The latents are
+    also scaled by kv_scale and the queries by its inverse, which keeps the
+    scores: the partials' power-of-two scale per row and feature half must
+    keep 1e4-sized and 1e-6-sized outputs as exact as unit ones, where plain
+    fp16 would overflow (past 65504) or go subnormal (below 6e-5)."""
+    if shape == "few_keys":
+        tree_lens, prefix, heads, splits, q_std = [8, 256, 28], [0, 0, 0], 64, 3, 0.5
+    else:
+        tree_lens, prefix, heads, splits, q_std = [64, 33], [700, 2000], 16, 40, 2.0
+    cfg = get_config("b1_h64_p4096_t16_bf16", batch=len(tree_lens), heads=heads, tree_nodes=max(tree_lens),
+                     prefix=0, tree_kind="uniform", q_std=q_std / kv_scale, kv_std=kv_scale, seed=71)
+    x = make_inputs(cfg, tree_lens=np.array(tree_lens), prefix_lens=np.array(prefix))
+    log("case %s kv_scale=%g splits=%d" % (shape, kv_scale, splits))
+    o, lse, info = run_hip(x, splits)
+    assert info["uses_combine"] == 1
+    o_ref, lse_ref = run_oracle(x)
+    assert np.abs(o_ref).max() > 2.0 * kv_scale  # outputs of a latent value's size
+    compare(o / kv_scale, lse, o_ref / kv_scale, lse_ref, "bf16", "plan=%s" % info)

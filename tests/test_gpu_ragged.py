@@ -498,3 +498,45 @@ def test_split_partials_of_latent_size(shape, kv_scale):
     o_ref, lse_ref = run_oracle(x)
     assert np.abs(o_ref).max() > 2.0 * kv_scale  # outputs of a latent value's size
     compare(o / kv_scale, lse, o_ref / kv_scale, lse_ref, "bf16", "plan=%s" % info)
+
+
+def test_random_shapes_sweep_wide():
+    """A wider random sweep (fixed seed, 120 problems), every element against
+    the oracle: 1..128 heads, prefixes up to 20,000 keys (none at all in some
+    problems, so rows see only their ancestors), tree sizes up to 256, branch
+    factors 1..4, paged or contiguous KV, and forced splits up to 40 (past 8
+    split groups per row, the lane-group combine). The oracle's work is capped
+    at 2e7 (row, key) pairs per problem by halving the prefixes, then the
+    trees. Its problems 57, 71 and 103 are the ones bf16-rounded split
+    partials failed (1.52e-2 .. 1.75e-2 against the 1.5e-2 bound)."""
+    rng = np.random.default_rng(1900)
+    for case in range(120):
+        dtype = "bf16" if case % 4 else "f32"
+        batch = int(rng.integers(1, 9))
+        heads = int(rng.choice([1, 2, 7, 16, 64, 128]))
+        tmax = int(rng.choice([1, 2, 16, 63, 64, 128, 200, 256]))
+        tree_lens = rng.integers(0, tmax + 1, size=batch)
+        tree_lens[int(rng.integers(0, batch))] = tmax
+        prefix = rng.integers(0, int(rng.choice([0, 100, 1000, 5000, 20000])) + 1, size=batch)
+        while int((tree_lens * heads * (prefix + tree_lens)).sum()) > 20_000_000 and prefix.max() > 0:
+            prefix = prefix // 2
+        while int((tree_lens * heads * (prefix + tree_lens)).sum()) > 20_000_000 and tree_lens.max() > 1:
+            tree_lens = np.maximum(tree_lens // 2, 1)
+        tmax = int(tree_lens.max())
+        kind = str(rng.choice(["uniform", "bounded", "chain"]))
+        paged = bool(rng.integers(0, 2))
+        splits = int(rng.choice([0, 0, 0, 1, 3, 8, 9, 16, 40]))
+        total = int((prefix + tree_lens).sum())
+        over = dict(batch=batch, heads=heads, tree_nodes=max(tmax, 1), dtype=dtype, tree_kind=kind,
+                    max_depth=300, max_branch=int(rng.integers(1, 5)), seed=6900 + case)
+        if paged:
+            cfg = get_config("b8_h64_paged600k_t16_bf16", prefix_range=(0, 1), pool_slots=total + 101, **over)
+        else:
+            cfg = get_config("b1_h64_p4096_t16_bf16", prefix=0, **over)
+        x = make_inputs(cfg, tree_lens=tree_lens, prefix_lens=prefix, poison_unused=paged)
+        log("wide sweep case %d: %s B=%d H=%d T_b=%s P=%s %s splits=%d %s" % (
+            case, dtype, batch, heads, tree_lens.tolist(), prefix.tolist(), kind, splits,
+            "paged" if paged else "contiguous"))
+        o, lse, info = run_hip(x, splits)
+        o_ref, lse_ref = run_oracle(x)
+        compare(o, lse, o_ref, lse_ref, dtype, "plan=%s" % info)

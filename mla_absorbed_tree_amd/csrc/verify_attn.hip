@@ -410,15 +410,16 @@ __host__ __device__ constexpr bool schedule_ok() {
 static_assert(schedule_ok(), "operand read schedule");
 static_assert(kRing > kPvHead, "the pre-barrier reads fit the ring");
 // Slots (MFMA indices) of the other work of an iteration: the loads of tile
-// t+2 (one part every third QK MFMA, the page-table block with the first),
+// t+2 (one part every third MFMA from the second, the page-table block with
+// the first),
 // the softmax of tile t+1 (after its last QK MFMA has left the pipe), the
 // hand-over of its weights to the partner, and the address preparation of
 // tile t+3's loads.
-constexpr int kDmaSlot0 = kQk0 + 2, kDmaStride = 3;
+constexpr int kDmaSlot0 = 1, kDmaStride = 3;
 constexpr int kSoftmaxSlot0 = kQk0 + kQkOps;
 constexpr int kSoftmaxSteps = 26;
 constexpr int kPrepSlots[3] = {kQk0 + kQkOps + 1, kQk0 + kQkOps + 12, kQk0 + kQkOps + 22};
-static_assert(kDmaSlot0 + kDmaStride * 8 < kQk0 + kQkOps, "loads go out during QK");
+static_assert(kDmaSlot0 + kDmaStride * 8 < kQk0 + kQkOps, "loads go out before the softmax");
 static_assert(kSoftmaxSlot0 + kSoftmaxSteps <= kOps, "softmax fits the PV MFMAs");
 }  // namespace bf16k
 
@@ -1001,10 +1002,14 @@ mla_verify_attn_bf16_kernel(const VerifyArgs a) {
           } else {
             mfma_qk(sacc, ring[o.r % kRing], qreg[o.c - 4]);
           }
-          // Tile t+2 goes into the buffer tile t-1 used; its addresses were
-          // prepared during the previous iteration. One load every few QK
-          // MFMAs (a burst of all of them from every wave queues in the
-          // vector-memory path and stalls the issuing waves).
+          // Tile t+2 goes into the buffer tile t-1 used, free since every
+          // wave passed the barrier; its addresses were prepared during the
+          // previous iteration. One load every third MFMA from the start of
+          // the iteration: a burst of all of them from every wave queues in
+          // the vector-memory path and stalls the issuing waves, and the
+          // earlier they go out, the more of their latency the iteration
+          // hides (page_size=1 pools, whose tiles miss L2 more often, gained
+          // 2.5-4% over loads that started at the third QK MFMA).
           if constexpr (s >= kDmaSlot0 && (s - kDmaSlot0) % kDmaStride == 0 &&
                         (s - kDmaSlot0) / kDmaStride < kTileParts) {
             constexpr int part = (s - kDmaSlot0) / kDmaStride;

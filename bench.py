@@ -78,17 +78,22 @@ def algorithmic_counts(x):
     return flops, bytes_, kv_tokens, pairs
 
 
-def bench_workload(name, steps, warmup, num_splits=None):
+def bench_workload(name, steps, warmup, num_splits=None, inputs=None):
+    """Time the workload's step; `inputs` = (x, device tensors) of an earlier
+    call on the same workload, to skip generating them again."""
     import torch
     from gen import get_config, make_inputs
     from mla_absorbed_tree_amd import binding as B
     from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
 
     cfg = get_config(name)
-    log("[bench] generating %s" % name)
-    x = make_inputs(cfg)
+    if inputs is None:
+        log("[bench] generating %s" % name)
+        x = make_inputs(cfg)
+        d = device_inputs(x)
+    else:
+        x, d = inputs
     flops, bytes_, kv_tokens, pairs = algorithmic_counts(x)
-    d = device_inputs(x)
     splits = cfg.num_splits if num_splits is None else num_splits
     ragged = x.parents.ndim == 1
     mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, x.kv_lens, splits,
@@ -401,6 +406,34 @@ def cpu_baseline(x, budget_s=15.0, single_budget_s=5.0):
     return res
 
 
+def split_sweep(name, counts, steps, warmup):
+    """The step time with the planner's automatic split counts (num_splits = 0)
+    against forced counts (the same number for every sequence, capped at its
+    key tiles), on the same inputs: a check of the planner's cost model. Two
+    passes over the list (the first configuration of a process runs a few per
+    cent slow); each configuration keeps its faster pass."""
+    from mla_absorbed_tree_amd.verify import device_inputs
+    from gen import get_config, make_inputs
+    log("[bench] generating %s" % name)
+    x = make_inputs(get_config(name))
+    inputs = (x, device_inputs(x))
+    configs = [0] + counts
+    rows = [None] * len(configs)
+    for rep in range(2):
+        for i, n in enumerate(configs):
+            r, _ = bench_workload(name, steps, warmup, n, inputs=inputs)
+            row = {"num_splits": n if n else "auto", "total_splits": r["plan"]["total_splits"],
+                   "total_groups": r["plan"]["total_groups"], "ms_per_step": r["ms_per_step"],
+                   "attention_ms": r["kernels_ms"]["attention"], "combine_ms": r["kernels_ms"]["combine"]}
+            log("[bench] %s pass %d splits=%s total=%d step %.4f ms" % (name, rep, row["num_splits"],
+                                                                       row["total_splits"], row["ms_per_step"]))
+            if rows[i] is None or row["ms_per_step"] < rows[i]["ms_per_step"]:
+                rows[i] = row
+    best = min(rows, key=lambda q: q["ms_per_step"])
+    print(json.dumps({"split_sweep": name, "steps": steps, "warmup": warmup, "rows": rows,
+                      "auto_over_best": rows[0]["ms_per_step"] / best["ms_per_step"]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +445,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compact", action="store_true", help="skip the KV-compaction measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--split-sweep", default="", metavar="N1,N2,...",
+                    help="only time --workload with the planner's split counts and with each forced "
+                         "count per sequence, one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (reference for HBM counters)")
     a = ap.parse_args()
@@ -429,6 +465,10 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if a.split_sweep:
+        split_sweep(a.workload, [int(n) for n in a.split_sweep.split(",")], a.steps, a.warmup)
+        return
 
     res, x = bench_workload(a.workload, a.steps, a.warmup, a.num_splits)
     also = []

@@ -20,25 +20,31 @@ std::string fmt(const char* f, long long a = 0, long long b = 0) {
 // tile. Split groups are dealt round-robin to the XCDs, all row blocks of a
 // group on one XCD and in order (as map_block does); each XCD runs one
 // workgroup per compute unit at a time and hands the next one, in dispatch
-// order, to the first unit that frees up. A workgroup costs its split's tiles
+// order, to the first unit that frees up. A workgroup costs its group's tiles
 // plus a fixed start-up (Q and tree loads, pipeline fill, epilogue). Split
 // partials add their write and the combine's read at HBM speed.
 constexpr double kWgOverheadTiles = 4.0;
 constexpr double kTileSeconds = 1.75e-6;      // one tile of one 128-row workgroup (measured)
 constexpr double kHbmBytesPerSecond = 5.0e12; // sustained partial write/read rate
 
+// S_b splits of sequence b cover its tiles in near-equal ranges (split s:
+// tiles s*T/S .. (s+1)*T/S - 1), and each split group runs `group`
+// consecutive splits in one workgroup per row block.
 double estimate_launch(const std::vector<int64_t>& tiles, const std::vector<int64_t>& row_blocks,
-                       const std::vector<int32_t>& splits, int rows_per_block, int dtype) {
+                       const std::vector<int32_t>& splits, int rows_per_block, int dtype, int64_t group = 1) {
   const int cus_per_xcd = kComputeUnits / kXcds;
   std::vector<std::vector<double>> free_at(kXcds, std::vector<double>(cus_per_xcd, 0.0));
   int64_t cg = 0;
   double partial_bytes = 0.0;
-  const double part_row_bytes = dtype == MLA_DTYPE_BF16 ? kDl * 2 + 8 : kDl * 4 + 8;
+  // (m, l, s0, s1) record and O: scaled fp16 for bf16 problems, fp32 for fp32
+  const double part_row_bytes = dtype == MLA_DTYPE_BF16 ? kDl * 2 + 16 : kDl * 4 + 16;
   for (size_t b = 0; b < tiles.size(); ++b) {
     const int64_t S = splits[b];
-    if (S > 1) partial_bytes += double(S) * double(row_blocks[b]) * rows_per_block * part_row_bytes;
-    for (int64_t s = 0; s < S; ++s, ++cg) {
-      const int64_t nt = (s + 1) * tiles[b] / S - s * tiles[b] / S;
+    const int64_t G = (S + group - 1) / group;
+    if (G > 1) partial_bytes += double(G) * double(row_blocks[b]) * rows_per_block * part_row_bytes;
+    for (int64_t c = 0; c < G; ++c, ++cg) {
+      const int64_t s0 = c * group, s1 = std::min(S, s0 + group);
+      const int64_t nt = s1 * tiles[b] / S - s0 * tiles[b] / S;
       std::vector<double>& cu = free_at[cg % kXcds];
       for (int64_t rb = 0; rb < row_blocks[b]; ++rb) {
         auto it = std::min_element(cu.begin(), cu.end());
@@ -49,6 +55,37 @@ double estimate_launch(const std::vector<int64_t>& tiles, const std::vector<int6
   double makespan = 0.0;
   for (const auto& cu : free_at) makespan = std::max(makespan, *std::max_element(cu.begin(), cu.end()));
   return makespan * kTileSeconds + 2.0 * partial_bytes / kHbmBytesPerSecond;
+}
+
+// Group size for forced split counts: the number of consecutive splits one
+// workgroup runs, chosen by the same estimate. For each group count G of the
+// longest sequence (S splits), from one group upwards, the candidate is the
+// smallest size that gives G groups, ceil(S / G), so that the groups come out
+// as even as they can; a candidate with more groups must beat the best so far
+// by 1% (ties keep fewer groups and fewer partials). Candidates whose
+// workgroups exceed kMaxSearchWorkgroups beyond the first are not tried, as
+// for automatic splits.
+int64_t choose_group(const std::vector<int64_t>& tiles, const std::vector<int64_t>& row_blocks,
+                     const std::vector<int32_t>& splits, int rows_per_block, int dtype) {
+  constexpr int64_t kMaxSearchWorkgroups = 16 * kComputeUnits;
+  const int64_t max_s = splits.empty() ? 1 : std::max<int64_t>(1, *std::max_element(splits.begin(), splits.end()));
+  int64_t best_g = max_s, first_n = -1, last_g = -1;
+  double best_t = -1.0;
+  for (int64_t G = 1; G <= max_s; ++G) {
+    const int64_t g = (max_s + G - 1) / G;
+    if (g == last_g) continue;  // the same partition of the longest sequence
+    last_g = g;
+    int64_t n = 0;
+    for (size_t b = 0; b < splits.size(); ++b) n += (splits[b] + g - 1) / g * row_blocks[b];
+    if (first_n < 0) first_n = n;
+    else if (n > first_n + kMaxSearchWorkgroups) break;
+    const double t = estimate_launch(tiles, row_blocks, splits, rows_per_block, dtype, g);
+    if (best_t < 0.0 || t < 0.99 * best_t) {
+      best_t = t;
+      best_g = g;
+    }
+  }
+  return best_g;
 }
 
 // Automatic split counts: candidate chunk lengths ceil(max_tiles / k),
@@ -228,18 +265,15 @@ mla_status build_plan(const mla_verify_problem& p, Plan& plan, std::string& err)
   plan.total_splits = plan.split_offset[p.batch];
   // Many short splits (a forced split count) would make thousands of
   // workgroups that each pay the fixed start-up and tail; instead one
-  // workgroup runs several consecutive splits, aiming at about one workgroup
-  // per compute unit. Its splits share one reference max, so their partials
-  // merge by a plain sum, done in the kernel's accumulators: the group writes
-  // one partial, and the combine merges the groups. The bf16 kernel only (the
-  // fp32 kernel runs one split per workgroup); automatic splits are already
-  // sized for the chip (one split each).
+  // workgroup runs several consecutive splits (a split group), as many as the
+  // launch-time estimate favours. Its splits share one reference max, so
+  // their partials merge by a plain sum, done in the kernel's accumulators:
+  // the group writes one partial, and the combine merges the groups. The bf16
+  // kernel only (the fp32 kernel runs one split per workgroup); automatic
+  // splits are already sized for the chip (one split each).
   plan.group = 1;
-  if (p.dtype == MLA_DTYPE_BF16 && p.num_splits > 0) {
-    int64_t split_row_blocks = 0;
-    for (int b = 0; b < p.batch; ++b) split_row_blocks += int64_t(plan.splits[b]) * row_blocks[b];
-    plan.group = int32_t(std::max<int64_t>(1, split_row_blocks / kComputeUnits));
-  }
+  if (p.dtype == MLA_DTYPE_BF16 && p.num_splits > 0)
+    plan.group = int32_t(choose_group(tiles, row_blocks, plan.splits, plan.rows_per_block, p.dtype));
   plan.group = std::min(plan.group, std::max(1, plan.max_splits));
   plan.group_offset.assign(p.batch + 1, 0);
   for (int b = 0; b < p.batch; ++b)

@@ -77,13 +77,27 @@ def test_forced_and_auto_split_schedules(B):
     # and the output in scaled fp16
     assert 16 * rows * (4 * 4 + 512 * 2) <= ws < 17 * rows * (4 * 4 + 512 * 2)
     B.mla_verify_plan_destroy(p)
-    # groups that do not divide the split counts: 3 splits per workgroup,
-    # ceil(40/3) + ceil(32/3) + ceil(40/3) = 14 + 11 + 14 groups, padded to 8 XCDs
-    p, _ = B.mla_verify_plan(3, 64, 16, 1, [3016, 1016, 1516], num_splits=40)
+    # groups that do not divide the split counts: 64, 32 and 48 splits (the
+    # last two capped at the key tiles) of 8 row blocks each; the estimate
+    # takes 6 splits per workgroup, ceil(64/6) + ceil(32/6) + ceil(48/6) =
+    # 11 + 6 + 8 = 25 groups (200 workgroups, one round), padded to 4 per XCD
+    p, _ = B.mla_verify_plan(3, 64, 16, 1, [3016, 1016, 1516], num_splits=64)
     info = B.mla_verify_plan_get_info(p)
-    assert info["total_splits"] == 40 + 32 + 40 and info["splits_per_workgroup"] == 3
-    assert info["grid_blocks"] == 40 * 8
+    assert info["total_splits"] == 64 + 32 + 48 and info["splits_per_workgroup"] == 6
+    assert info["total_groups"] == 25 and info["grid_blocks"] == 4 * 8 * 8
     B.mla_verify_plan_destroy(p)
+    # forced splits on the ragged batch (T_b = 172, 207, 6, 207 at 64 heads:
+    # 86, 104, 3 and 104 row blocks of 32,800-odd keys). A rule that aimed at
+    # one workgroup per compute unit merged every forced count into one group
+    # per sequence there: 4 groups for 8 XCDs, 104 row blocks queued on one
+    # XCD's 32 units, 6.3 ms against 2.3 ms measured. The estimate keeps every
+    # XCD busy: one split per group up to 8 per sequence, then 32 groups.
+    tl = [172, 207, 6, 207]
+    for ns, groups in ((2, 8), (4, 16), (8, 32), (16, 32), (64, 32)):
+        p, _ = B.mla_verify_plan(4, 64, 256, 1, [32768 + t for t in tl], num_splits=ns, tree_len_host=tl)
+        info = B.mla_verify_plan_get_info(p)
+        assert info["total_splits"] == 4 * ns and info["total_groups"] == groups, (ns, info)
+        B.mla_verify_plan_destroy(p)
     # fp32 problems run one split per workgroup
     p, _ = B.mla_verify_plan(1, 64, 32, 0, [200032], num_splits=256)
     assert B.mla_verify_plan_get_info(p)["splits_per_workgroup"] == 1

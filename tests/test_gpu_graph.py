@@ -89,8 +89,8 @@ def test_one_plan_and_graph_across_decode_steps():
     """One plan and one captured graph serve two decode steps whose lengths,
     slot tables, trees and queries change in place on the device. The second
     step's middle sequence is far shorter than planned, so 45 of its 48 splits
-    get no keys; each workgroup runs 4 splits, so empty splits also sit inside
-    groups that have keys."""
+    get no keys (splits 0..2 keep theirs); each workgroup runs several splits
+    (6 here), so empty splits also sit inside a group that has keys."""
     import dataclasses
     from gpu_util import compare, run_oracle
     from mla_absorbed_tree_amd.verify import MlaVerify, device_inputs
@@ -98,7 +98,7 @@ def test_one_plan_and_graph_across_decode_steps():
     steps = [make_inputs(cfg, prefix_lens=np.array([1800, 1600, 2000])),
              make_inputs(dataclasses.replace(cfg, seed=41), prefix_lens=np.array([1900, 60, 2100]))]
     mv = MlaVerify(cfg.batch, cfg.heads, cfg.tree_nodes, cfg.dtype, steps[0].kv_lens, 48)
-    assert mv.info["splits_per_workgroup"] == 4, mv.info
+    assert 3 < mv.info["splits_per_workgroup"] < 48, mv.info
     d = device_inputs(steps[0])
     cap = max(len(x.kv_indices) for x in steps)
     idx = torch.zeros(cap, dtype=torch.int32, device="cuda")

@@ -192,7 +192,7 @@ def test_planning_large_batches_is_fast(B):
 def test_plans_of_the_named_workloads(B):
     """The planner's choices for the measured workloads (a change here changes
     what the benchmark measures, so it should be deliberate)."""
-    from gen import get_config, make_inputs
+    from gen import get_config
     want = {"tiny_f32_b1_h16_p256_t8": (2, 32, 1), "b1_h64_p4096_t16_bf16": (17, 192, 1),
             "b4_h64_p32768_t64_bf16": (8, 256, 1), "b1_h64_p200000_t32_bf16_s256": (256, 256, 16),
             "b8_h64_paged600k_t16_bf16": (64, 512, 1), "b4_h64_p32768_t1to256_ragged_bf16": (32, 3328, 1)}

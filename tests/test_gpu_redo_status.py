@@ -17,7 +17,7 @@ import pytest
 
 from gen import get_config, make_inputs
 from gen.inputs import round_to_bf16
-from gpu_util import compare, log, node_rows, run_hip, run_oracle
+from gpu_util import compare, log, run_hip, run_oracle
 
 pytestmark = pytest.mark.gpu
 

@@ -9,7 +9,6 @@ with a causal mask, a boolean transitive closure, and a planted dominant key.
 """
 import numpy as np
 import pytest
-import torch
 
 from gen import make_tree_parents
 from oracle import brute_force_verify, tree_mask_words, verify_attention

@@ -5,7 +5,7 @@ in a row, the second on a smaller problem, each compared with mla_verify_run
 import numpy as np
 import pytest
 
-from gpu_util import TOL, compare, log, run_oracle
+from gpu_util import compare, log, run_oracle
 
 pytestmark = pytest.mark.gpu
 

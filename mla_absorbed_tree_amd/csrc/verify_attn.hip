@@ -431,7 +431,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // compiler's own wait insertion does not treat every later LDS read as
 // dependent on them (which would drain the whole prefetch ring); the kernel
 // waits for them explicitly with wait_vmem<>. Vector-memory loads retire in
-// order, so the compiler's waits for its own loads stay correct.
+// order, so the compiler's waits for its own loads stay correct. Each asm
+// block sets M0 (the LDS destination) and lists it as clobbered; the compiler
+// reserves M0 and warns that it will not restore a value of its own around
+// the block. It keeps none: the generated code of this file uses M0 only
+// inside these blocks (a CPU test checks the assembly, implicit uses
+// included).
 
 // The page-table entries of this wave's 8 keys of tiles 8B..8B+7 (batch B >=
 // 0), lane i fetching key i%8 of tile 8B + i/8 into ring half B % 2 (one

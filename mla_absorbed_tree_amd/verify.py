@@ -41,9 +41,9 @@ class MlaVerify:
             self.tables = torch.empty(self.info["table_bytes"] // 4, dtype=torch.int32, device=device)
             B.mla_verify_plan_stage_tables(self.plan, self.tables)
 
-    def __call__(self, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents, scale,
-                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 stream=None):
+    def _check(self, q_nope, q_pe, kv_c, k_pe, int_tensors, out, lse):
+        """Dtype, device and shape checks the C ABI cannot make (it sees bare
+        pointers); returns (out, lse), allocated when not given."""
         rows = self.nodes
         for name, t in (("q_nope", q_nope), ("q_pe", q_pe), ("kv_c", kv_c), ("k_pe", k_pe)):
             if t.dtype != self.torch_dtype or not t.is_cuda:
@@ -52,16 +52,48 @@ class MlaVerify:
             raise ValueError("q_nope must be contiguous [nodes, H, 512]")
         if tuple(q_pe.shape) != (rows, self.heads, 64) or not q_pe.is_contiguous():
             raise ValueError("q_pe must be contiguous [nodes, H, 64]")
-        for name, t in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("tree_parents", tree_parents)):
+        for name, t in int_tensors:
             if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
                 raise TypeError("%s must be a contiguous int32 device tensor" % name)
         if out is None:
             out = torch.empty((rows, self.heads, 512), dtype=torch.float32, device=q_nope.device)
+        elif (out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous()
+              or tuple(out.shape) != (rows, self.heads, 512)):
+            raise ValueError("out must be a contiguous float32 device tensor [nodes, H, 512]")
         if lse is None:
             lse = torch.empty((rows, self.heads), dtype=torch.float32, device=q_nope.device)
+        elif (lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous()
+              or tuple(lse.shape) != (rows, self.heads)):
+            raise ValueError("lse must be a contiguous float32 device tensor [nodes, H]")
+        return out, lse
+
+    def __call__(self, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents, scale,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 stream=None):
+        out, lse = self._check(q_nope, q_pe, kv_c, k_pe, (("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
+                                                          ("tree_parents", tree_parents)), out, lse)
         B.mla_verify_run(self.plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_parents,
                          scale, out, lse, self.workspace, self.workspace.numel(), stream)
         return out, lse
+
+    def varlen(self, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_indptr, tree_parents, scale,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+        """mla_verify_run_varlen: the tree packing is read from the device
+        tree_indptr [batch+1] at run time, each size within the plan's. The
+        buffers hold the plan's node total, which bounds tree_indptr[batch]
+        when tree_indptr[0] = 0; rows past tree_indptr[batch] are not written."""
+        out, lse = self._check(q_nope, q_pe, kv_c, k_pe, (("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
+                                                          ("tree_indptr", tree_indptr),
+                                                          ("tree_parents", tree_parents)), out, lse)
+        B.mla_verify_run_varlen(self.plan, q_nope, q_pe, kv_c, k_pe, kv_indptr, kv_indices, tree_indptr,
+                                tree_parents, scale, out, lse, self.workspace, self.workspace.numel(), stream)
+        return out, lse
+
+    def status(self) -> torch.Tensor:
+        """The per-sequence status words of the last run (int32 [batch],
+        MLA_VERIFY_STATUS_* bits, 0 = valid): a view of the workspace, so
+        synchronise the run's stream before reading it on the host."""
+        return self.workspace[: 4 * self.batch].view(torch.int32)
 
     def close(self):
         if self.plan is not None:

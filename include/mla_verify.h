@@ -250,10 +250,11 @@ mla_status mla_verify_run_noalloc(mla_verify_plan_t plan, const void* q_nope, co
  * splits_per_workgroup consecutive KV splits of one row block, which share
  * one reference max, so their merge is a plain sum kept in the workgroup's
  * accumulators. Sequences with a single split group write out/lse directly;
- * the others leave one partial per split group in the workspace: (m, l) in
- * fp32, and the group's unnormalised output O = l * o_group: fp32 for fp32
- * problems; for bf16 problems fp16 times a power of two per row and feature
- * half (kept in the row's fp32 record), which moves the result by at most
+ * the others leave one partial per split group in the workspace: an fp32
+ * record per row (m, l and two scales), and the group's unnormalised output
+ * O = l * o_group: fp32 for fp32 problems; for bf16 problems fp16 times a
+ * power of two per row and feature half (its inverse is one of the record's
+ * scales), which moves the result by at most
  * 2^-12 of that half's largest |o_group| (bf16 storage would move each
  * element by up to 2^-9 of itself, about 8e-3 where a row's weight sits on
  * a few keys with latent values near 4).

@@ -179,7 +179,8 @@ mla_status mla_verify_plan_stage_tables(mla_verify_plan_t plan, void* tables, si
  *               token; parent[t] < t.  A node whose parent chain is invalid gets
  *               NaN output rows and lse.
  *   scale       softmax scale applied to the summed dot products; positive
- *               and finite (MLA_ERR_INVALID_ARG otherwise)
+ *               and below 2.3e38, so that scale * log2(e) is finite
+ *               (MLA_ERR_INVALID_ARG otherwise)
  *   out         device fp32 [nodes, H, 512]
  *   lse         device fp32 [nodes, H] (natural log) or NULL
  *   workspace   device, >= workspace_bytes of the plan, 256-byte aligned.  Holds

@@ -120,8 +120,9 @@ mla_status prepare(mla_verify_plan_t plan, const void* q_nope, const void* q_pe,
                                        " bytes is smaller than the plan's " + std::to_string(p.ws_bytes));
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (need_inputs && !(scale > 0.f && scale < 3.0e38f))
-    return fail(MLA_ERR_INVALID_ARG, "scale must be positive and finite");
+  // The kernels work with scale * log2(e), which must be finite too.
+  if (need_inputs && !(scale > 0.f && scale < 2.3e38f))
+    return fail(MLA_ERR_INVALID_ARG, "scale must be positive and finite (below 2.3e38)");
 
   std::memset(&a, 0, sizeof a);
   a.q_nope = q_nope;

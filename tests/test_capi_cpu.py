@@ -142,7 +142,7 @@ def test_run_argument_checks_happen_before_any_launch(B):
     with pytest.raises(B.MlaVerifyError) as e:
         B.mla_verify_run(p, *args, float("nan"), fake, fake, fake, ws, stream=0)
     assert e.value.status == B.MLA_ERR_INVALID_ARG
-    for bad in (0.0, -0.5, float("inf")):
+    for bad in (0.0, -0.5, float("inf"), 2.5e38):  # the last overflows scale * log2(e)
         with pytest.raises(B.MlaVerifyError) as e:
             B.mla_verify_run(p, *args, bad, fake, fake, fake, ws, stream=0)
         assert e.value.status == B.MLA_ERR_INVALID_ARG

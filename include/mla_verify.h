@@ -174,6 +174,9 @@ mla_status mla_verify_plan_stage_tables(mla_verify_plan_t plan, void* tables, si
  *   kv_indices  device int32 [kv_indptr[batch]]: slot of logical position j of
  *               sequence b at kv_indices[kv_indptr[b] + j] (page_size = 1).
  *               Positions 0..P_b-1 are the prefix, P_b..P_b+T_b-1 the tree nodes.
+ *               The library does not know the pool's size: every entry must be
+ *               a slot of kv_c and k_pe (0 <= s < slots), or the kernels read
+ *               outside them.
  *   tree_parents device int32 [nodes]: parent of packed node node_off[b] + t as
  *               a node index of the same tree, -1 = child of the last prefix
  *               token; parent[t] < t.  A node whose parent chain is invalid gets
